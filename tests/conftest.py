@@ -1,0 +1,28 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an AMD Instinct GPU (gfx950) and the built HIP library")
+
+
+def pytest_collection_modifyitems(config, items):
+    # GPU tests are skipped, not failed, where torch sees no GPU; the GPU run
+    # selects them with -m gpu on a machine that has one.
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        has_gpu = False
+    if has_gpu:
+        return
+    skip = pytest.mark.skip(reason="no GPU visible to torch")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)
