@@ -1,0 +1,168 @@
+/*
+ * arrms.h - fused rank-partial sum + residual add + RMSNorm on one AMD Instinct
+ * MI355X (gfx950), as a C ABI.
+ *
+ * The operation is the contract of the page "[TLERaw] Add NVSHMEM allreduce
+ * RMSNorm tutorial" (FlagTree PR #1122), section Summary, restated in section
+ * Implementation 3 ("Residual + RMSNorm epilogue"):
+ *
+ *     reduced      = sum over W rank partials of x
+ *     residual_out = reduced + residual
+ *     norm_out     = RMSNorm(residual_out, weight, eps)
+ *
+ * on BF16 token rows (section Correctness: BF16, hidden size 2048, world size 4),
+ * with token rows mapped to independent workgroups (section Implementation 2,
+ * "Row-parallel execution").  The W rank partials are W BF16 buffers already
+ * resident in this GPU's memory (for example landed there by peer copies); this
+ * library moves no data between GPUs.
+ *
+ * Arithmetic, per element h of token row t (identical in every variant):
+ *   acc  = x_0[t][h] + x_1[t][h] + ... + x_{W-1}[t][h]   binary32, rank order
+ *   red  = bf16(acc)                                     round to nearest even
+ *   ro   = bf16(red + residual[t][h])                    -> residual_out
+ *   inv  = (float)(1 / sqrt(sum_h ro^2 / H + eps))       binary64, rounded once
+ *   norm = bf16((ro * inv) * weight[h])                  -> norm_out
+ *
+ * Layout: every [T][H] tensor is BF16 (16-bit bfloat) row-major with row
+ * stride H elements; weight is BF16 [H]; eps is binary32.  All pointers are
+ * device pointers on the handle's device unless stated otherwise.
+ *
+ * Ownership: the caller owns every tensor.  A handle owns only its split-H
+ * workspace.  Calls are asynchronous on the caller's stream: no host
+ * synchronisation, no internal streams, no allocation after arrms_create.
+ *
+ * Threading: a handle may have at most one arrms_fused in flight at a time
+ * (the split-H variant uses the handle's workspace).  Use one handle per
+ * stream for concurrent streams.
+ */
+#ifndef ARRMS_H
+#define ARRMS_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes -------------------------------------------------------- */
+#define ARRMS_OK 0
+#define ARRMS_ERR_INVALID_ARG 1 /* bad pointer, size, eps, alignment or aliasing */
+#define ARRMS_ERR_UNSUPPORTED 2 /* a valid request the selected variant cannot run */
+#define ARRMS_ERR_HIP 3         /* a HIP call failed; see arrms_last_hip_error */
+#define ARRMS_ERR_OOM 4         /* workspace allocation failed in arrms_create */
+
+/* ---- kernel variants ----------------------------------------------------- */
+#define ARRMS_VARIANT_AUTO 0   /* choose per call from the shape (default) */
+#define ARRMS_VARIANT_ROW 1    /* one token row per workgroup (or per lane group) */
+#define ARRMS_VARIANT_SPLITH 2 /* each row split over several workgroups, two phases */
+#define ARRMS_VARIANT_SCALAR 3 /* element-wise loads: any H, any 2-byte alignment */
+
+#define ARRMS_MAX_WORLD 16        /* largest W */
+#define ARRMS_MAX_HIDDEN 65536    /* largest H */
+#define ARRMS_ROW_MAX_HIDDEN 16384 /* largest H of the row variant */
+
+typedef struct arrms_ctx* arrms_handle_t;
+
+/* Launch plan of one call, as chosen by arrms_plan / arrms_query_plan. */
+typedef struct {
+    int variant;         /* ARRMS_VARIANT_ROW, _SPLITH or _SCALAR (0 when tokens == 0) */
+    int grid;            /* workgroups launched (0: nothing is launched) */
+    int block;           /* threads per workgroup */
+    int vec_per_thread;  /* 16-byte vectors per lane per input (row, split-H); 0 for scalar */
+    int threads_per_row; /* lanes sharing one row (row) or one chunk (split-H) */
+    int rows_per_block;  /* token rows per workgroup (row), else 1 */
+    int chunks_per_row;  /* split-H chunks per row (split-H), else 1 */
+} arrms_plan_t;
+
+/* Optional tuning overrides; 0 (or -1 where stated) keeps the automatic choice. */
+typedef struct {
+    int vec_per_thread;    /* row / split-H: 1, 2, 4 or 8 */
+    int threads_per_row;   /* row: 16, 32 or a multiple of 64 up to 1024 */
+    int splith_block;      /* split-H: threads per workgroup, 64..1024, multiple of 64 */
+    int splith_max_tokens; /* automatic variant uses split-H when tokens <= this; -1 automatic */
+} arrms_tuning_t;
+
+/*
+ * Create a handle bound to HIP device `device`.
+ *   max_world  : largest W a call will pass, 1..ARRMS_MAX_WORLD
+ *   max_tokens : largest T a call will pass, >= 0
+ *   max_hidden : largest H a call will pass, 1..ARRMS_MAX_HIDDEN
+ * Reads the device's compute-unit count, allocates and zeroes the split-H
+ * workspace (max_tokens * ceil(max_hidden / 512) doubles plus max_tokens
+ * 32-bit tickets), and reads the environment variable ARRMS_FORCE_VARIANT
+ * (row | splith | scalar) once.  All one-time work happens here.
+ * Returns ARRMS_OK and *out, or ARRMS_ERR_INVALID_ARG (bad limits, out NULL),
+ * ARRMS_ERR_HIP (no such device) or ARRMS_ERR_OOM; *out is NULL on error.
+ * Synchronous: the workspace is zeroed before it returns.
+ */
+int arrms_create(arrms_handle_t* out, int device, int max_world, int max_tokens, int max_hidden);
+
+/*
+ * Enqueue the fused operator on `stream` (0 = the null stream of the handle's device).
+ *   partials     : HOST array of `world` device pointers, each BF16 [tokens][hidden];
+ *                  read at call time, the caller may free the array on return
+ *   world        : W, 1..max_world
+ *   tokens       : T, 0..max_tokens (0: returns ARRMS_OK, enqueues nothing)
+ *   hidden       : H, 1..max_hidden
+ *   residual     : BF16 [tokens][hidden]
+ *   weight       : BF16 [hidden]
+ *   eps          : finite, >= 0
+ *   residual_out : BF16 [tokens][hidden] output; may be exactly `residual` (in place)
+ *   norm_out     : BF16 [tokens][hidden] output
+ * Pointers must be 2-byte aligned.  Outputs may not overlap each other or any
+ * input, except residual_out == residual.  Inputs may overlap each other.
+ * H a multiple of 8 with every pointer 16-byte aligned uses the vector kernels;
+ * anything else uses the scalar kernel with the same results.
+ * All checks happen before anything is enqueued: an error has no side effect.
+ * Returns ARRMS_OK, ARRMS_ERR_INVALID_ARG, ARRMS_ERR_UNSUPPORTED (a forced
+ * variant cannot run this shape) or ARRMS_ERR_HIP (launch failure).
+ */
+int arrms_fused(arrms_handle_t h, const void* const* partials, int world, int tokens, int hidden,
+                const void* residual, const void* weight, float eps, void* residual_out,
+                void* norm_out, hipStream_t stream);
+
+/*
+ * Free the handle's workspace and the handle.  NULL is accepted (ARRMS_OK).
+ * The caller must make sure no call on the handle is still executing
+ * (synchronise its stream first).  Using a destroyed handle is undefined.
+ */
+int arrms_destroy(arrms_handle_t h);
+
+/* Static text for a status code ("unknown status" for others). */
+const char* arrms_status_string(int status);
+
+/* hipError_t of the last failed HIP call on this handle (0 if none; -1 for a NULL handle). */
+int arrms_last_hip_error(arrms_handle_t h);
+
+/* Force a variant (ARRMS_VARIANT_*) for later calls; AUTO restores per-shape choice.
+ * Returns ARRMS_ERR_INVALID_ARG for an unknown variant or NULL handle. */
+int arrms_set_variant(arrms_handle_t h, int variant);
+
+/* Set (tuning != NULL) or clear (NULL) tuning overrides; checked like arrms_plan. */
+int arrms_set_tuning(arrms_handle_t h, const arrms_tuning_t* tuning);
+
+/*
+ * Host-only validation and launch planning, exactly as arrms_fused does it,
+ * without touching any device: pointers are compared, never dereferenced.
+ *   cu_count  : compute units of the device (256 on MI355X)
+ *   variant   : ARRMS_VARIANT_* (AUTO chooses)
+ *   tuning    : overrides or NULL
+ *   max_*     : the limits a handle was created with
+ * Other arguments as for arrms_fused.  Fills *plan and returns the status
+ * arrms_fused would return before launching.
+ */
+int arrms_plan(int cu_count, int variant, const arrms_tuning_t* tuning, int max_world,
+               int max_tokens, int max_hidden, const void* const* partials, int world, int tokens,
+               int hidden, const void* residual, const void* weight, float eps,
+               const void* residual_out, const void* norm_out, arrms_plan_t* plan);
+
+/* arrms_plan with the handle's device, limits, forced variant and tuning. */
+int arrms_query_plan(arrms_handle_t h, const void* const* partials, int world, int tokens,
+                     int hidden, const void* residual, const void* weight, float eps,
+                     const void* residual_out, const void* norm_out, arrms_plan_t* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARRMS_H */

@@ -1,0 +1,406 @@
+// C ABI of the fused rank-partial sum + residual add + RMSNorm library
+// (declared in include/arrms.h): handle lifecycle, argument validation,
+// variant selection and launch on the caller's stream.
+//
+// The page "[TLERaw] Add NVSHMEM allreduce RMSNorm tutorial" (FlagTree PR #1122),
+// section Implementation 4, gives its host side an init / workspace / cleanup
+// life cycle behind a C ABI; here the one-time work (device query, workspace
+// allocation and zeroing, reading the variant override) happens in
+// arrms_create only, and arrms_fused does no allocation and no synchronisation.
+#include "arrms.h"
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "arrms_internal.h"
+
+struct arrms_ctx {
+    int device;
+    int cu_count;
+    int max_world;
+    int max_tokens;
+    int max_hidden;
+    int variant;  // forced variant, ARRMS_VARIANT_AUTO for per-shape choice
+    bool has_tuning;
+    arrms_tuning_t tuning;
+    int ws_chunks;  // chunks per row the workspace holds
+    double* ws;
+    unsigned* tickets;
+    int last_hip_error;
+};
+
+namespace {
+
+// Smallest split-H chunk: one wave of 16-byte vectors (512 BF16 elements).
+constexpr int kMinChunkVec = 64;
+// Largest (W + 2) * vectors-per-lane the row variant keeps in registers.
+constexpr int kMaxLiveVectors = 40;
+
+int chunks_capacity(int max_hidden) {
+    const int nvec = (max_hidden + 7) / 8;
+    return (nvec + kMinChunkVec - 1) / kMinChunkVec;
+}
+
+// Register-array extent of the rank loop: specialised W, else the generic 16.
+int world_extent(int world) { return (world <= 8 || world == 16) ? world : arrms::kMaxWorld; }
+
+// Must match the __launch_bounds__ of the row kernels.
+int row_max_threads(int world, int vpt) {
+    if (world_extent(world) > 8) return vpt == 1 ? 512 : 256;
+    return vpt == 1 ? 1024 : (vpt <= 4 ? 512 : 256);
+}
+
+int round_threads(int n) {
+    if (n <= 16) return 16;
+    if (n <= 32) return 32;
+    return (n + 63) / 64 * 64;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a);
+    const uintptr_t y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+bool valid_tuning(const arrms_tuning_t* t) {
+    if (!t) return true;
+    const int v = t->vec_per_thread;
+    if (!(v == 0 || v == 1 || v == 2 || v == 4 || v == 8)) return false;
+    const int r = t->threads_per_row;
+    if (!(r == 0 || r == 16 || r == 32 || (r > 0 && r % 64 == 0 && r <= 1024))) return false;
+    const int b = t->splith_block;
+    if (!(b == 0 || (b > 0 && b % 64 == 0 && b <= 1024))) return false;
+    if (t->splith_max_tokens < -1) return false;
+    return true;
+}
+
+// Row variant plan; returns ARRMS_ERR_UNSUPPORTED when the shape or the
+// tuning overrides do not fit the row kernels.
+int plan_row(int world, int tokens, int hidden, const arrms_tuning_t* t, arrms_plan_t* p) {
+    const int nvec = hidden / 8;
+    const int we = world_extent(world);
+    int best_vpt = 0, best_tpr = 0;
+    long best_waste = 0;
+    for (int vpt = 1; vpt <= 8; vpt *= 2) {
+        if (t && t->vec_per_thread && t->vec_per_thread != vpt) continue;
+        if ((we + 2) * vpt > kMaxLiveVectors) continue;
+        int tpr = round_threads((nvec + vpt - 1) / vpt);
+        if (t && t->threads_per_row) tpr = t->threads_per_row;
+        if (tpr > row_max_threads(world, vpt) || static_cast<long>(tpr) * vpt < nvec) continue;
+        const long waste = static_cast<long>(tpr) * vpt - nvec;
+        // least idle vector slots, then the row group closest to 256 lanes
+        if (!best_vpt || waste < best_waste ||
+            (waste == best_waste && abs(tpr - 256) < abs(best_tpr - 256))) {
+            best_vpt = vpt;
+            best_tpr = tpr;
+            best_waste = waste;
+        }
+    }
+    if (!best_vpt) return ARRMS_ERR_UNSUPPORTED;
+    int rpb = best_tpr < 256 ? 256 / best_tpr : 1;
+    while (rpb > 1 && best_tpr * rpb > row_max_threads(world, best_vpt)) rpb /= 2;
+    p->variant = ARRMS_VARIANT_ROW;
+    p->vec_per_thread = best_vpt;
+    p->threads_per_row = best_tpr;
+    p->rows_per_block = rpb;
+    p->chunks_per_row = 1;
+    p->block = best_tpr * rpb;
+    p->grid = (tokens + rpb - 1) / rpb;
+    return ARRMS_OK;
+}
+
+// Split-H plan.  Aims at about two workgroups per compute unit over the whole
+// call, with chunks of at least one wave of vectors.
+int plan_splith(int cu_count, int max_hidden, int world, int tokens, int hidden,
+                const arrms_tuning_t* t, arrms_plan_t* p) {
+    const int nvec = hidden / 8;
+    const int cap = chunks_capacity(max_hidden);
+    int vpt = (t && t->vec_per_thread) ? t->vec_per_thread : 1;
+    const int max_block = world_extent(world) > 8 ? 512 : 1024;  // split-H __launch_bounds__
+    if (vpt > 2) return ARRMS_ERR_UNSUPPORTED;
+    if (world_extent(world) > 8 && vpt > 1) return ARRMS_ERR_UNSUPPORTED;
+    int block;
+    if (t && t->splith_block) {
+        block = t->splith_block;
+    } else {
+        const long want_wgs = 2L * cu_count;
+        long chunks = (want_wgs + tokens - 1) / tokens;
+        const long max_chunks = (nvec + kMinChunkVec - 1) / kMinChunkVec;
+        if (chunks > max_chunks) chunks = max_chunks;
+        if (chunks < 1) chunks = 1;
+        const long chunk_vec = (nvec + chunks - 1) / chunks;
+        block = static_cast<int>((chunk_vec + vpt - 1) / vpt);
+        block = (block + 63) / 64 * 64;
+        if (block > max_block) {
+            vpt = (world_extent(world) > 8) ? 1 : 2;
+            block = static_cast<int>((chunk_vec + vpt - 1) / vpt);
+            block = (block + 63) / 64 * 64;
+            if (block > max_block) block = max_block;
+        }
+    }
+    if (block > max_block) return ARRMS_ERR_UNSUPPORTED;
+    const int chunk_vec = block * vpt;
+    const int chunks = (nvec + chunk_vec - 1) / chunk_vec;
+    if (chunks > cap) return ARRMS_ERR_UNSUPPORTED;
+    if (static_cast<long>(tokens) * chunks > 0x7fffffffL) return ARRMS_ERR_UNSUPPORTED;
+    p->variant = ARRMS_VARIANT_SPLITH;
+    p->vec_per_thread = vpt;
+    p->threads_per_row = block;
+    p->rows_per_block = 1;
+    p->chunks_per_row = chunks;
+    p->block = block;
+    p->grid = tokens * chunks;
+    return ARRMS_OK;
+}
+
+void plan_scalar(int tokens, int hidden, arrms_plan_t* p) {
+    int block = (hidden + 63) / 64 * 64;
+    if (block > 256) block = 256;
+    p->variant = ARRMS_VARIANT_SCALAR;
+    p->vec_per_thread = 0;
+    p->threads_per_row = block;
+    p->rows_per_block = 1;
+    p->chunks_per_row = 1;
+    p->block = block;
+    p->grid = tokens;
+}
+
+// Automatic crossover to split-H: rows that leave most compute units idle.
+int auto_splith_max_tokens(int cu_count, int hidden) {
+    (void)hidden;
+    return cu_count / 8;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* arrms_status_string(int status) {
+    switch (status) {
+        case ARRMS_OK: return "ok";
+        case ARRMS_ERR_INVALID_ARG: return "invalid argument";
+        case ARRMS_ERR_UNSUPPORTED: return "unsupported shape or variant";
+        case ARRMS_ERR_HIP: return "HIP runtime error";
+        case ARRMS_ERR_OOM: return "out of device memory";
+        default: return "unknown status";
+    }
+}
+
+int arrms_plan(int cu_count, int variant, const arrms_tuning_t* tuning, int max_world, int max_tokens,
+               int max_hidden, const void* const* partials, int world, int tokens, int hidden,
+               const void* residual, const void* weight, float eps, const void* residual_out,
+               const void* norm_out, arrms_plan_t* plan) {
+    if (!plan) return ARRMS_ERR_INVALID_ARG;
+    memset(plan, 0, sizeof *plan);
+    if (cu_count < 1 || max_world < 1 || max_world > ARRMS_MAX_WORLD || max_tokens < 0 ||
+        max_hidden < 1 || max_hidden > ARRMS_MAX_HIDDEN)
+        return ARRMS_ERR_INVALID_ARG;
+    if (variant < ARRMS_VARIANT_AUTO || variant > ARRMS_VARIANT_SCALAR) return ARRMS_ERR_INVALID_ARG;
+    if (!valid_tuning(tuning)) return ARRMS_ERR_INVALID_ARG;
+    if (world < 1 || world > max_world) return ARRMS_ERR_INVALID_ARG;
+    if (tokens < 0 || tokens > max_tokens) return ARRMS_ERR_INVALID_ARG;
+    if (hidden < 1 || hidden > max_hidden) return ARRMS_ERR_INVALID_ARG;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return ARRMS_ERR_INVALID_ARG;
+    if (tokens == 0) return ARRMS_OK;  // nothing to do, nothing enqueued
+
+    if (!partials || !residual || !weight || !residual_out || !norm_out) return ARRMS_ERR_INVALID_ARG;
+    for (int r = 0; r < world; ++r)
+        if (!partials[r]) return ARRMS_ERR_INVALID_ARG;
+
+    // BF16 element alignment of every pointer.
+    uintptr_t any = reinterpret_cast<uintptr_t>(residual) | reinterpret_cast<uintptr_t>(weight) |
+                    reinterpret_cast<uintptr_t>(residual_out) | reinterpret_cast<uintptr_t>(norm_out);
+    for (int r = 0; r < world; ++r) any |= reinterpret_cast<uintptr_t>(partials[r]);
+    if (any & 1u) return ARRMS_ERR_INVALID_ARG;
+
+    // Aliasing: outputs overlap nothing, except residual_out == residual exactly.
+    const size_t n = static_cast<size_t>(tokens) * static_cast<size_t>(hidden) * 2;
+    const size_t nw = static_cast<size_t>(hidden) * 2;
+    if (overlap(residual_out, n, norm_out, n)) return ARRMS_ERR_INVALID_ARG;
+    if (residual_out != residual && overlap(residual_out, n, residual, n)) return ARRMS_ERR_INVALID_ARG;
+    if (overlap(norm_out, n, residual, n)) return ARRMS_ERR_INVALID_ARG;
+    if (overlap(residual_out, n, weight, nw) || overlap(norm_out, n, weight, nw)) return ARRMS_ERR_INVALID_ARG;
+    for (int r = 0; r < world; ++r)
+        if (overlap(residual_out, n, partials[r], n) || overlap(norm_out, n, partials[r], n))
+            return ARRMS_ERR_INVALID_ARG;
+
+    const bool vector_ok = (hidden % 8 == 0) && ((any & 15u) == 0);
+    switch (variant) {
+        case ARRMS_VARIANT_SCALAR:
+            plan_scalar(tokens, hidden, plan);
+            return ARRMS_OK;
+        case ARRMS_VARIANT_ROW:
+            if (!vector_ok || hidden > ARRMS_ROW_MAX_HIDDEN) return ARRMS_ERR_UNSUPPORTED;
+            return plan_row(world, tokens, hidden, tuning, plan);
+        case ARRMS_VARIANT_SPLITH:
+            if (!vector_ok) return ARRMS_ERR_UNSUPPORTED;
+            return plan_splith(cu_count, max_hidden, world, tokens, hidden, tuning, plan);
+        default:
+            break;
+    }
+    if (!vector_ok) {
+        plan_scalar(tokens, hidden, plan);
+        return ARRMS_OK;
+    }
+    int split_max = (tuning && tuning->splith_max_tokens >= 0) ? tuning->splith_max_tokens
+                                                              : auto_splith_max_tokens(cu_count, hidden);
+    if (hidden > ARRMS_ROW_MAX_HIDDEN || tokens <= split_max) {
+        const int rc = plan_splith(cu_count, max_hidden, world, tokens, hidden, tuning, plan);
+        if (rc == ARRMS_OK || hidden > ARRMS_ROW_MAX_HIDDEN) return rc;
+        memset(plan, 0, sizeof *plan);
+    }
+    if (plan_row(world, tokens, hidden, tuning, plan) == ARRMS_OK) return ARRMS_OK;
+    // A row the row kernels cannot hold in registers: split it, else go element-wise.
+    memset(plan, 0, sizeof *plan);
+    if (plan_splith(cu_count, max_hidden, world, tokens, hidden, tuning, plan) == ARRMS_OK) return ARRMS_OK;
+    memset(plan, 0, sizeof *plan);
+    plan_scalar(tokens, hidden, plan);
+    return ARRMS_OK;
+}
+
+int arrms_create(arrms_handle_t* out, int device, int max_world, int max_tokens, int max_hidden) {
+    if (!out) return ARRMS_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (max_world < 1 || max_world > ARRMS_MAX_WORLD || max_tokens < 0 || max_hidden < 1 ||
+        max_hidden > ARRMS_MAX_HIDDEN || device < 0)
+        return ARRMS_ERR_INVALID_ARG;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || device >= count) return ARRMS_ERR_HIP;
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cu < 1)
+        return ARRMS_ERR_HIP;
+
+    arrms_ctx* h = new (std::nothrow) arrms_ctx();
+    if (!h) return ARRMS_ERR_OOM;
+    h->device = device;
+    h->cu_count = cu;
+    h->max_world = max_world;
+    h->max_tokens = max_tokens;
+    h->max_hidden = max_hidden;
+    h->variant = ARRMS_VARIANT_AUTO;
+    h->ws_chunks = chunks_capacity(max_hidden);
+
+    const char* force = getenv("ARRMS_FORCE_VARIANT");
+    if (force) {
+        if (!strcmp(force, "row")) h->variant = ARRMS_VARIANT_ROW;
+        else if (!strcmp(force, "splith")) h->variant = ARRMS_VARIANT_SPLITH;
+        else if (!strcmp(force, "scalar")) h->variant = ARRMS_VARIANT_SCALAR;
+    }
+
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (hipSetDevice(device) != hipSuccess) {
+        delete h;
+        return ARRMS_ERR_HIP;
+    }
+    int rc = ARRMS_OK;
+    const size_t rows = max_tokens > 0 ? static_cast<size_t>(max_tokens) : 1;
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&h->ws), rows * h->ws_chunks * sizeof(double));
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&h->tickets), rows * sizeof(unsigned));
+    if (e == hipSuccess) e = hipMemset(h->tickets, 0, rows * sizeof(unsigned));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) rc = (e == hipErrorOutOfMemory) ? ARRMS_ERR_OOM : ARRMS_ERR_HIP;
+    if (rc != ARRMS_OK) {
+        if (h->ws) (void)hipFree(h->ws);
+        if (h->tickets) (void)hipFree(h->tickets);
+        delete h;
+        h = nullptr;
+    }
+    if (prev >= 0 && prev != device) (void)hipSetDevice(prev);
+    *out = h;
+    return rc;
+}
+
+int arrms_destroy(arrms_handle_t h) {
+    if (!h) return ARRMS_OK;
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    (void)hipSetDevice(h->device);
+    int rc = ARRMS_OK;
+    if (h->ws && hipFree(h->ws) != hipSuccess) rc = ARRMS_ERR_HIP;
+    if (h->tickets && hipFree(h->tickets) != hipSuccess) rc = ARRMS_ERR_HIP;
+    if (prev >= 0 && prev != h->device) (void)hipSetDevice(prev);
+    delete h;
+    return rc;
+}
+
+int arrms_last_hip_error(arrms_handle_t h) { return h ? h->last_hip_error : -1; }
+
+int arrms_set_variant(arrms_handle_t h, int variant) {
+    if (!h || variant < ARRMS_VARIANT_AUTO || variant > ARRMS_VARIANT_SCALAR) return ARRMS_ERR_INVALID_ARG;
+    h->variant = variant;
+    return ARRMS_OK;
+}
+
+int arrms_set_tuning(arrms_handle_t h, const arrms_tuning_t* tuning) {
+    if (!h || !valid_tuning(tuning)) return ARRMS_ERR_INVALID_ARG;
+    h->has_tuning = tuning != nullptr;
+    if (tuning) h->tuning = *tuning;
+    return ARRMS_OK;
+}
+
+int arrms_query_plan(arrms_handle_t h, const void* const* partials, int world, int tokens, int hidden,
+                     const void* residual, const void* weight, float eps, const void* residual_out,
+                     const void* norm_out, arrms_plan_t* plan) {
+    if (!h) {
+        if (plan) memset(plan, 0, sizeof *plan);
+        return ARRMS_ERR_INVALID_ARG;
+    }
+    return arrms_plan(h->cu_count, h->variant, h->has_tuning ? &h->tuning : nullptr, h->max_world,
+                      h->max_tokens, h->max_hidden, partials, world, tokens, hidden, residual, weight, eps,
+                      residual_out, norm_out, plan);
+}
+
+int arrms_fused(arrms_handle_t h, const void* const* partials, int world, int tokens, int hidden,
+                const void* residual, const void* weight, float eps, void* residual_out, void* norm_out,
+                hipStream_t stream) {
+    arrms_plan_t p;
+    const int rc = arrms_query_plan(h, partials, world, tokens, hidden, residual, weight, eps, residual_out,
+                                    norm_out, &p);
+    if (rc != ARRMS_OK || p.grid == 0) return rc;
+
+    arrms::Args a;
+    memset(&a, 0, sizeof a);
+    for (int r = 0; r < world; ++r) a.x.p[r] = partials[r];
+    a.residual = residual;
+    a.weight = weight;
+    a.residual_out = residual_out;
+    a.norm_out = norm_out;
+    a.ws = h->ws;
+    a.tickets = h->tickets;
+    a.hidden_d = static_cast<double>(hidden);
+    a.eps = eps;
+    a.world = world;
+    a.tokens = tokens;
+    a.hidden = hidden;
+    a.nvec = hidden / 8;
+    a.threads_per_row = p.threads_per_row;
+    a.rows_per_block = p.rows_per_block;
+    a.chunks = p.chunks_per_row;
+    a.chunk_vec = p.block * p.vec_per_thread;
+
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != h->device && hipSetDevice(h->device) != hipSuccess) {
+        h->last_hip_error = static_cast<int>(hipErrorInvalidDevice);
+        return ARRMS_ERR_HIP;
+    }
+    hipError_t e;
+    switch (p.variant) {
+        case ARRMS_VARIANT_ROW: e = arrms::launch_row(a, p.vec_per_thread, p.grid, p.block, stream); break;
+        case ARRMS_VARIANT_SPLITH: e = arrms::launch_splith(a, p.vec_per_thread, p.grid, p.block, stream); break;
+        default: e = arrms::launch_scalar(a, p.grid, p.block, stream); break;
+    }
+    if (prev >= 0 && prev != h->device) (void)hipSetDevice(prev);
+    if (e != hipSuccess) {
+        h->last_hip_error = static_cast<int>(e);
+        return ARRMS_ERR_HIP;
+    }
+    return ARRMS_OK;
+}
+
+}  // extern "C"

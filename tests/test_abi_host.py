@@ -1,0 +1,195 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and its
+host-only validation and variant planning (arrms_plan) behave as include/arrms.h says.
+No kernel is launched and no device memory is touched: pointers are fake integers
+that the planner compares but never dereferences."""
+import os
+import re
+
+import pytest
+
+import residual_add_rmsnorm_arrms_amd as A
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "arrms.h")
+CU = 256
+LIM = dict(max_world=16, max_tokens=20000, max_hidden=65536)
+BASE = 0x7F0000000000
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    if not os.path.exists(A.LIB_PATH):
+        from residual_add_rmsnorm_arrms_amd import build
+        build.build()
+    return A.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(arrms_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    assert sorted(A.EXPORTS) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert A.arrms_status_string(A.ARRMS_OK) == "ok"
+    assert A.arrms_status_string(A.ARRMS_ERR_INVALID_ARG) == "invalid argument"
+    assert A.arrms_status_string(A.ARRMS_ERR_UNSUPPORTED) == "unsupported shape or variant"
+    assert A.arrms_status_string(A.ARRMS_ERR_HIP) == "HIP runtime error"
+    assert A.arrms_status_string(A.ARRMS_ERR_OOM) == "out of device memory"
+    assert A.arrms_status_string(99) == "unknown status"
+
+
+def bufs(W, T, H, align=256, off=0):
+    """Disjoint fake buffers: W partials, residual, weight, residual_out, norm_out."""
+    n = T * H * 2
+    step = (n + 2 * H + 4096 + align - 1) // align * align
+    ptrs = [BASE + i * step + off for i in range(W + 4)]
+    return dict(partials=ptrs[:W], residual=ptrs[W], weight=ptrs[W + 1], residual_out=ptrs[W + 2],
+                norm_out=ptrs[W + 3])
+
+
+def plan(W, T, H, variant=A.ARRMS_VARIANT_AUTO, tuning=None, eps=1e-6, cu=CU, lim=LIM, **over):
+    b = bufs(W, T, H)
+    b.update(over)
+    return A.arrms_plan(cu, variant, tuning, lim["max_world"], lim["max_tokens"], lim["max_hidden"],
+                        b["partials"], W, T, H, b["residual"], b["weight"], eps, b["residual_out"], b["norm_out"])
+
+
+def test_prefill_shape_uses_row_variant():
+    rc, p = plan(4, 4096, 2048)
+    assert rc == A.ARRMS_OK
+    assert p["variant"] == A.ARRMS_VARIANT_ROW
+    assert p["threads_per_row"] * p["vec_per_thread"] >= 2048 // 8
+    assert p["grid"] * p["rows_per_block"] >= 4096
+    assert p["block"] % 64 == 0 and p["block"] <= 1024
+
+
+@pytest.mark.parametrize("W,T,H", [(8, 8192, 8192), (8, 16383, 5120), (2, 4, 128), (4, 1000, 64), (1, 5, 8),
+                                   (16, 300, 2048), (11, 300, 4096), (3, 77, 16384)])
+def test_row_plans_cover_the_row(W, T, H):
+    rc, p = plan(W, T, H, variant=A.ARRMS_VARIANT_ROW)
+    assert rc == A.ARRMS_OK, (W, T, H)
+    nvec = H // 8
+    assert p["threads_per_row"] * p["vec_per_thread"] >= nvec
+    assert p["grid"] * p["rows_per_block"] >= T > (p["grid"] - 1) * p["rows_per_block"]
+    assert p["block"] == p["threads_per_row"] * p["rows_per_block"] and p["block"] % 64 == 0
+    assert p["threads_per_row"] in (16, 32) or p["threads_per_row"] % 64 == 0
+    we = W if (W <= 8 or W == 16) else 16
+    assert (we + 2) * p["vec_per_thread"] <= 40
+
+
+@pytest.mark.parametrize("W,T,H", [(4, 1, 2048), (4, 16, 2048), (8, 1, 8192), (8, 3, 65536), (16, 2, 2048),
+                                   (4, 5000, 32768), (12, 1, 24576)])
+def test_splith_plans(W, T, H):
+    rc, p = plan(W, T, H, variant=A.ARRMS_VARIANT_SPLITH)
+    assert rc == A.ARRMS_OK, (W, T, H)
+    chunk = p["block"] * p["vec_per_thread"]
+    assert p["chunks_per_row"] == -(-(H // 8) // chunk)
+    assert p["chunks_per_row"] <= -(-(65536 // 8) // 64)
+    assert p["grid"] == T * p["chunks_per_row"]
+    assert p["block"] % 64 == 0 and p["block"] <= (512 if W > 8 else 1024)
+
+
+def test_auto_selection():
+    assert plan(4, 1, 2048)[1]["variant"] == A.ARRMS_VARIANT_SPLITH      # decode: few rows
+    assert plan(4, 4096, 2048)[1]["variant"] == A.ARRMS_VARIANT_ROW      # prefill
+    assert plan(4, 4096, 32768)[1]["variant"] == A.ARRMS_VARIANT_SPLITH  # H beyond the row kernels
+    assert plan(4, 100, 1000)[1]["variant"] == A.ARRMS_VARIANT_ROW       # H % 8 == 0
+    assert plan(4, 100, 1001)[1]["variant"] == A.ARRMS_VARIANT_SCALAR    # H % 8 != 0
+    b = bufs(4, 100, 2048)
+    rc, p = plan(4, 100, 2048, residual=b["residual"] + 2)               # 2-byte aligned only
+    assert rc == A.ARRMS_OK and p["variant"] == A.ARRMS_VARIANT_SCALAR
+    t = A.arrms_tuning_t(0, 0, 0, 0)
+    assert plan(4, 1, 2048, tuning=t)[1]["variant"] == A.ARRMS_VARIANT_ROW  # crossover forced to 0
+
+
+def test_forced_variant_unsupported():
+    assert plan(4, 10, 1000 + 1, variant=A.ARRMS_VARIANT_ROW)[0] == A.ARRMS_ERR_UNSUPPORTED
+    assert plan(4, 10, 1001, variant=A.ARRMS_VARIANT_SPLITH)[0] == A.ARRMS_ERR_UNSUPPORTED
+    assert plan(4, 10, 32768, variant=A.ARRMS_VARIANT_ROW)[0] == A.ARRMS_ERR_UNSUPPORTED
+    assert plan(4, 10, 1001, variant=A.ARRMS_VARIANT_SCALAR)[0] == A.ARRMS_OK
+    t = A.arrms_tuning_t(8, 0, 0, -1)
+    assert plan(8, 10, 2048, variant=A.ARRMS_VARIANT_ROW, tuning=t)[0] == A.ARRMS_ERR_UNSUPPORTED  # registers
+
+
+def test_tokens_zero_is_ok_and_plans_nothing():
+    rc, p = A.arrms_plan(CU, 0, None, 4, 10, 2048, None, 4, 0, 2048, 0, 0, 1e-6, 0, 0)
+    assert rc == A.ARRMS_OK and p["grid"] == 0
+
+
+@pytest.mark.parametrize("case", [
+    dict(W=0), dict(W=17), dict(T=-1), dict(T=20001), dict(H=0), dict(H=65537),
+    dict(eps=-1e-6), dict(eps=float("nan")), dict(eps=float("inf")),
+    dict(cu=0), dict(variant=4), dict(variant=-1),
+])
+def test_invalid_sizes(case):
+    W, T, H = case.get("W", 4), case.get("T", 16), case.get("H", 2048)
+    b = bufs(max(W, 1), max(T, 1), max(H, 1))
+    parts = (b["partials"] * 17)[:max(W, 1)]
+    rc, p = A.arrms_plan(case.get("cu", CU), case.get("variant", 0), None, 16, 20000, 65536, parts, W, T, H,
+                         b["residual"], b["weight"], case.get("eps", 1e-6), b["residual_out"], b["norm_out"])
+    assert rc == A.ARRMS_ERR_INVALID_ARG and p["grid"] == 0
+
+
+def test_world_above_handle_limit():
+    lim = dict(LIM, max_world=4)
+    assert plan(5, 16, 2048, lim=lim)[0] == A.ARRMS_ERR_INVALID_ARG
+    assert plan(4, 16, 2048, lim=lim)[0] == A.ARRMS_OK
+
+
+@pytest.mark.parametrize("field", ["residual", "weight", "residual_out", "norm_out"])
+def test_null_pointers(field):
+    assert plan(4, 16, 2048, **{field: 0})[0] == A.ARRMS_ERR_INVALID_ARG
+
+
+def test_null_partial_and_odd_alignment():
+    b = bufs(4, 16, 2048)
+    assert plan(4, 16, 2048, partials=[b["partials"][0], 0, *b["partials"][2:]])[0] == A.ARRMS_ERR_INVALID_ARG
+    assert plan(4, 16, 2048, norm_out=b["norm_out"] + 1)[0] == A.ARRMS_ERR_INVALID_ARG
+    assert plan(4, 16, 2048, partials=[b["partials"][0] + 1, *b["partials"][1:]])[0] == A.ARRMS_ERR_INVALID_ARG
+
+
+def test_aliasing_rules():
+    b = bufs(4, 16, 2048)
+    n = 16 * 2048 * 2
+    assert plan(4, 16, 2048, residual_out=b["residual"])[0] == A.ARRMS_OK                # in place
+    assert plan(4, 16, 2048, residual_out=b["residual"] + 64)[0] == A.ARRMS_ERR_INVALID_ARG  # partial overlap
+    assert plan(4, 16, 2048, norm_out=b["residual_out"] + n - 2)[0] == A.ARRMS_ERR_INVALID_ARG
+    assert plan(4, 16, 2048, norm_out=b["residual_out"] + n)[0] == A.ARRMS_OK              # adjacent is fine
+    assert plan(4, 16, 2048, norm_out=b["residual"])[0] == A.ARRMS_ERR_INVALID_ARG
+    assert plan(4, 16, 2048, residual_out=b["partials"][2])[0] == A.ARRMS_ERR_INVALID_ARG
+    assert plan(4, 16, 2048, norm_out=b["weight"] - 2)[0] == A.ARRMS_ERR_INVALID_ARG
+    # inputs may overlap each other (read-only)
+    p = b["partials"]
+    assert plan(4, 16, 2048, partials=[p[0], p[0], p[0], p[0]])[0] == A.ARRMS_OK
+
+
+@pytest.mark.parametrize("t", [(3, 0, 0, -1), (0, 48, 0, -1), (0, 2048, 0, -1), (0, 0, 100, -1), (0, 0, 0, -2)])
+def test_invalid_tuning(t):
+    assert plan(4, 16, 2048, tuning=A.arrms_tuning_t(*t))[0] == A.ARRMS_ERR_INVALID_ARG
+
+
+def test_null_handle_calls():
+    assert A.arrms_destroy(None) == A.ARRMS_OK
+    assert A.arrms_last_hip_error(None) == -1
+    assert A.arrms_set_variant(None, 0) == A.ARRMS_ERR_INVALID_ARG
+    assert A.arrms_set_tuning(None, None) == A.ARRMS_ERR_INVALID_ARG
+    b = bufs(4, 16, 2048)
+    rc, p = A.arrms_query_plan(None, b["partials"], 4, 16, 2048, b["residual"], b["weight"], 1e-6,
+                               b["residual_out"], b["norm_out"])
+    assert rc == A.ARRMS_ERR_INVALID_ARG
+    assert A.arrms_fused(None, b["partials"], 4, 16, 2048, b["residual"], b["weight"], 1e-6, b["residual_out"],
+                         b["norm_out"], 0) == A.ARRMS_ERR_INVALID_ARG
+
+
+def test_create_rejects_bad_limits():
+    for args in [(0, 0, 16, 2048), (0, 17, 16, 2048), (0, 4, -1, 2048), (0, 4, 16, 0), (0, 4, 16, 65537),
+                 (-1, 4, 16, 2048)]:
+        rc, h = A.arrms_create(*args)
+        assert rc == A.ARRMS_ERR_INVALID_ARG and h is None

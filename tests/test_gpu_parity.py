@@ -1,0 +1,296 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle on the same
+seeded inputs, element by element.  See tests/gpu_util.py for the bar."""
+import numpy as np
+import pytest
+import torch
+
+import residual_add_rmsnorm_arrms_amd as A
+import synth
+from tests.bf16util import bf16_values
+from tests.gpu_util import assert_parity, inputs, op, reference, run, say
+
+pytestmark = pytest.mark.gpu
+
+ROW, SPLITH, SCALAR, AUTO = A.ARRMS_VARIANT_ROW, A.ARRMS_VARIANT_SPLITH, A.ARRMS_VARIANT_SCALAR, A.ARRMS_VARIANT_AUTO
+VNAME = {AUTO: "auto", ROW: "row", SPLITH: "splith", SCALAR: "scalar"}
+
+
+def parity(W, T, H, variant=AUTO, tuning=None, seed=0, sigma=1.0, eps=1e-6, outlier_p=0.0, inplace=False):
+    where = "W=%d T=%d H=%d variant=%s tuning=%s seed=%d inplace=%s" % (W, T, H, VNAME[variant], tuning, seed,
+                                                                         inplace)
+    say("case " + where)
+    x, res, w = inputs(W, T, H, seed=seed, sigma=sigma, eps=eps, outlier_p=outlier_p)
+    ro, no, plan = run(x, res, w, eps, variant=variant, tuning=tuning, inplace=inplace)
+    ref = reference(x, res, w, eps)
+    n = assert_parity(ro, no, ref, where)
+    say("  plan %s, norm_out not bit-identical: %d of %d" % (plan, n, no.size))
+    return plan, n
+
+
+# ------------------------------------------------------------ named workloads
+@pytest.mark.parametrize("name", ["tiny", "decode_t1", "decode_t16", "decode_t128", "prefill"])
+def test_named_workload(name):
+    wl = synth.WORKLOADS[name]
+    say("workload %s" % name)
+    x, res, w = synth.make_inputs(wl)
+    ro, no, plan = run(x, res, w, wl.eps)
+    n = assert_parity(ro, no, reference(x, res, w, wl.eps), name)
+    say("  plan %s, norm_out not bit-identical: %d of %d" % (plan, n, no.size))
+
+
+@pytest.mark.parametrize("name", ["large_hidden", "ragged_outliers"])
+def test_full_size_workload(name):
+    """Full-size workloads in the launch configuration the benchmark times (automatic
+    variant), every element compared with the oracle."""
+    wl = synth.WORKLOADS[name]
+    say("workload %s (full size, all %d rows)" % (name, wl.tokens))
+    x, res, w = synth.make_inputs(wl)
+    ro, no, plan = run(x, res, w, wl.eps)
+    ref = reference(x, res, w, wl.eps)
+    n = assert_parity(ro, no, ref, name)
+    say("  plan %s, norm_out not bit-identical: %d of %d" % (plan, n, no.size))
+
+
+# ------------------------------------------------------------ sweeps
+TOKENS = [1, 2, 3, 15, 16, 17, 63, 64, 127, 128, 255, 256, 257, 1024, 4096]
+
+
+@pytest.mark.parametrize("T", TOKENS)
+@pytest.mark.parametrize("variant", [AUTO, ROW, SPLITH, SCALAR])
+def test_token_sweep(T, variant):
+    if variant == SCALAR and T > 1024:
+        pytest.skip("scalar variant covered up to T=1024")
+    plan, _ = parity(4, T, 2048, variant=variant, seed=T)
+    if variant != AUTO:
+        assert plan["variant"] == variant
+
+
+HIDDEN = [8, 64, 128, 1000, 1001, 2040, 2048, 5120, 8192, 16384, 24576]
+
+
+@pytest.mark.parametrize("H", HIDDEN)
+@pytest.mark.parametrize("variant", [AUTO, ROW, SPLITH, SCALAR])
+def test_hidden_sweep(H, variant):
+    vector_ok = H % 8 == 0
+    if variant == ROW and (not vector_ok or H > A.ARRMS_ROW_MAX_HIDDEN):
+        pytest.skip("row variant needs H % 8 == 0 and H <= 16384")
+    if variant == SPLITH and not vector_ok:
+        pytest.skip("split-H variant needs H % 8 == 0")
+    parity(4, 37, H, variant=variant, seed=H)
+
+
+WORLDS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 16]
+
+
+@pytest.mark.parametrize("W", WORLDS)
+@pytest.mark.parametrize("variant", [AUTO, ROW, SPLITH, SCALAR])
+def test_world_sweep(W, variant):
+    parity(W, 33, 2048, variant=variant, seed=100 + W)
+
+
+def _row_tunings(W, H):
+    nvec = H // 8
+    out = []
+    for vpt in (1, 2, 4, 8):
+        we = W if (W <= 8 or W == 16) else 16
+        if (we + 2) * vpt > 40:
+            continue
+        for tpr in (16, 32, 64, 128, 192, 256, 320, 512, 640, 1024):
+            cap = (512 if vpt == 1 else 256) if we > 8 else (1024 if vpt == 1 else (512 if vpt <= 4 else 256))
+            if tpr * vpt >= nvec and tpr <= cap and tpr * vpt < 2 * nvec + 64:
+                out.append(dict(vec_per_thread=vpt, threads_per_row=tpr))
+    return out
+
+
+ROW_TUNING_CASES = [(W, H, t) for W, H in [(4, 2048), (8, 8192), (8, 5120), (2, 128), (3, 1000)]
+                    for t in _row_tunings(W, H)]
+
+
+@pytest.mark.parametrize("W,H,tuning", ROW_TUNING_CASES,
+                         ids=["W%d-H%d-v%d-t%d" % (W, H, t["vec_per_thread"], t["threads_per_row"])
+                              for W, H, t in ROW_TUNING_CASES])
+def test_row_tuning_grid(W, H, tuning):
+    """Every row-kernel instance and lane-group size the planner can pick or the benchmark
+    sweeps, on a ragged row count."""
+    plan, _ = parity(W, 67, H, variant=ROW, tuning=tuning, seed=7)
+    assert plan["vec_per_thread"] == tuning["vec_per_thread"]
+    assert plan["threads_per_row"] == tuning["threads_per_row"]
+
+
+SPLITH_CASES = [(W, H, b, v) for W, H in [(4, 2048), (8, 8192), (8, 5120), (16, 2048)]
+                for b in (64, 128, 256, 512, 1024) for v in (1, 2)
+                if not (W > 8 and (v > 1 or b > 512))]
+
+
+@pytest.mark.parametrize("W,H,block,vpt", SPLITH_CASES)
+def test_splith_tuning_grid(W, H, block, vpt):
+    plan, _ = parity(W, 5, H, variant=SPLITH, tuning=dict(vec_per_thread=vpt, splith_block=block), seed=9)
+    assert plan["block"] == block and plan["vec_per_thread"] == vpt
+
+
+# ------------------------------------------------------------ semantics and edge cases
+@pytest.mark.parametrize("variant", [ROW, SPLITH, SCALAR])
+def test_in_place_residual(variant):
+    parity(4, 130, 2048, variant=variant, inplace=True, seed=3)
+
+
+def test_misaligned_pointers_take_scalar_path():
+    say("case misaligned +2 bytes, W=3 T=21 H=2048")
+    W, T, H = 3, 21, 2048
+    x, res, w = inputs(W, T, H, seed=5)
+    dev = torch.device("cuda", 0)
+    n = T * H
+
+    def shifted(t):
+        buf = torch.zeros(t.numel() + 8, dtype=torch.bfloat16, device=dev)
+        view = buf[1:1 + t.numel()].view(t.shape)
+        view.copy_(t.to(dev))
+        return view
+
+    xs = [shifted(x[r]) for r in range(W)]
+    rs, ws = shifted(res), shifted(w)
+    ro = torch.zeros(n + 8, dtype=torch.bfloat16, device=dev)[1:1 + n].view(T, H)
+    no = torch.zeros(n + 8, dtype=torch.bfloat16, device=dev)[1:1 + n].view(T, H)
+    o = op()
+    assert o.plan(xs, rs, ws, 1e-6, ro, no)["variant"] == SCALAR
+    o(xs, rs, ws, 1e-6, ro, no)
+    torch.cuda.synchronize()
+    assert_parity(synth.bits(ro.cpu()), synth.bits(no.cpu()), reference(x, res, w, 1e-6), "misaligned")
+
+
+@pytest.mark.parametrize("variant", [ROW, SPLITH, SCALAR])
+def test_guard_bands_untouched(variant):
+    """Outputs sit between canary bands; no kernel writes outside its outputs."""
+    say("case guard bands variant=%s" % VNAME[variant])
+    W, T, H, G = 4, 77, 2048, 4096
+    x, res, w = inputs(W, T, H, seed=12)
+    dev = torch.device("cuda", 0)
+    canary = torch.full((2 * G + T * H,), 0x5A5A, dtype=torch.int16, device=dev)
+    ro_buf, no_buf = canary.clone(), canary.clone()
+    ro = ro_buf.view(torch.bfloat16)[G:G + T * H].view(T, H)
+    no = no_buf.view(torch.bfloat16)[G:G + T * H].view(T, H)
+    o = op()
+    o.set_variant(variant)
+    try:
+        o(x.to(dev), res.to(dev), w.to(dev), 1e-6, ro, no)
+        torch.cuda.synchronize()
+    finally:
+        o.set_variant(AUTO)
+    for buf in (ro_buf, no_buf):
+        b = buf.cpu()
+        assert bool((b[:G] == 0x5A5A).all()) and bool((b[G + T * H:] == 0x5A5A).all())
+    assert_parity(synth.bits(ro.cpu()), synth.bits(no.cpu()), reference(x, res, w, 1e-6), "guard")
+
+
+@pytest.mark.parametrize("variant", [AUTO, ROW, SPLITH, SCALAR])
+@pytest.mark.parametrize("T", [1, 16, 128])
+def test_deterministic(variant, T):
+    say("case determinism variant=%s T=%d" % (VNAME[variant], T))
+    x, res, w = inputs(4, T, 2048, seed=13)
+    first = run(x, res, w, 1e-6, variant=variant)
+    for _ in range(3):
+        again = run(x, res, w, 1e-6, variant=variant)
+        assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
+
+
+def test_splith_back_to_back_calls_reset_tickets():
+    """Many split-H calls in a row on one handle and stream, each on different data: the
+    arrival counters must return to zero after every call."""
+    say("case split-H back-to-back")
+    dev = torch.device("cuda", 0)
+    o = op()
+    cases = [inputs(4, T, 2048, seed=200 + T) for T in (1, 5, 16, 40, 128, 3)]
+    dev_in = [(x.to(dev), r.to(dev), w.to(dev)) for x, r, w in cases]
+    o.set_variant(SPLITH)
+    try:
+        outs = []
+        for rep in range(20):
+            for xd, rd, wd in dev_in:
+                outs.append(o(xd, rd, wd, 1e-6))
+        torch.cuda.synchronize()
+    finally:
+        o.set_variant(AUTO)
+    for i, (ro, no) in enumerate(outs[-len(cases):]):
+        x, r, w = cases[i]
+        assert_parity(synth.bits(ro.cpu()), synth.bits(no.cpu()), reference(x, r, w, 1e-6), "b2b %d" % i)
+    for i, (ro, no) in enumerate(outs[:len(cases)]):
+        x, r, w = cases[i]
+        assert_parity(synth.bits(ro.cpu()), synth.bits(no.cpu()), reference(x, r, w, 1e-6), "b2b first %d" % i)
+
+
+def test_zero_tokens_enqueues_nothing():
+    say("case T=0")
+    dev = torch.device("cuda", 0)
+    e = torch.empty((0, 2048), dtype=torch.bfloat16, device=dev)
+    w = torch.ones(2048, dtype=torch.bfloat16, device=dev)
+    rc = A.arrms_fused(op().handle, [e.data_ptr()] * 4, 4, 0, 2048, e.data_ptr(), w.data_ptr(), 1e-6,
+                       e.data_ptr(), e.data_ptr(), 0)
+    assert rc == A.ARRMS_OK
+
+
+@pytest.mark.parametrize("variant", [ROW, SPLITH, SCALAR])
+def test_zero_row_with_zero_eps_gives_nan_like_oracle(variant):
+    say("case zero rows eps=0 variant=%s" % VNAME[variant])
+    x, res, w = inputs(2, 9, 2048, seed=14)
+    x[:, 3] = 0
+    res[3] = 0
+    ro, no, _ = run(x, res, w, 0.0, variant=variant)
+    ref = reference(x, res, w, 0.0)
+    assert np.isnan(bf16_values(no[3])).all()
+    assert_parity(ro, no, ref, "zero-row eps=0")
+
+
+@pytest.mark.parametrize("variant", [ROW, SPLITH, SCALAR])
+def test_zero_residual_exposes_reduced(variant):
+    """With residual = 0, residual_out equals the BF16 rank sum `reduced` (by value)."""
+    say("case reduced via zero residual variant=%s" % VNAME[variant])
+    x, res, w = inputs(8, 50, 5120, seed=15, outlier_p=0.01)
+    res.zero_()
+    ro, no, _ = run(x, res, w, 1e-6, variant=variant)
+    ref = reference(x, res, w, 1e-6)
+    np.testing.assert_array_equal(bf16_values(ro), bf16_values(ref["reduced"]))
+    assert_parity(ro, no, ref, "zero residual")
+
+
+def test_non_default_stream():
+    say("case non-default stream")
+    s = torch.cuda.Stream(device=0)
+    x, res, w = inputs(4, 300, 2048, seed=16)
+    with torch.cuda.stream(s):
+        ro, no, _ = run(x, res, w, 1e-6, stream=s)
+    assert_parity(ro, no, reference(x, res, w, 1e-6), "stream")
+
+
+def test_errors_on_a_device_handle():
+    say("case error returns")
+    dev = torch.device("cuda", 0)
+    rc, h = A.arrms_create(0, 4, 8, 2048)
+    assert rc == A.ARRMS_OK
+    try:
+        t = torch.zeros((16, 4096), dtype=torch.bfloat16, device=dev)
+        w = torch.ones(4096, dtype=torch.bfloat16, device=dev)
+        p = t.data_ptr()
+        big = torch.zeros((3, 16, 4096), dtype=torch.bfloat16, device=dev)
+        q = [big[i].data_ptr() for i in range(3)]
+        ok = lambda W, T, H: (h, [p] * W, W, T, H, p, w.data_ptr(), 1e-6, q[1], q[2], 0)
+        assert A.arrms_fused(*ok(4, 8, 2048)) == A.ARRMS_OK
+        assert A.arrms_fused(*ok(5, 8, 2048)) == A.ARRMS_ERR_INVALID_ARG    # world > max_world
+        assert A.arrms_fused(*ok(4, 9, 2048)) == A.ARRMS_ERR_INVALID_ARG    # tokens > max_tokens
+        assert A.arrms_fused(*ok(4, 8, 4096)) == A.ARRMS_ERR_INVALID_ARG    # hidden > max_hidden
+        bad_eps = list(ok(4, 8, 2048))
+        bad_eps[7] = -1.0
+        assert A.arrms_fused(*bad_eps) == A.ARRMS_ERR_INVALID_ARG
+        torch.cuda.synchronize()
+        assert A.arrms_last_hip_error(h) == 0
+    finally:
+        assert A.arrms_destroy(h) == A.ARRMS_OK
+
+
+def test_create_destroy_cycles():
+    say("case create/destroy cycles")
+    for i in range(5):
+        rc, h = A.arrms_create(0, 8, 1000 + i, 8192)
+        assert rc == A.ARRMS_OK and h
+        assert A.arrms_destroy(h) == A.ARRMS_OK
+    rc, h = A.arrms_create(0, 4, 2 ** 31 - 1, 65536)  # workspace far beyond device memory
+    assert rc == A.ARRMS_ERR_OOM and h is None
