@@ -1,0 +1,398 @@
+"""Benchmark of the fused rank-partial sum + residual add + RMSNorm on one MI355X.
+
+Headline: W=4 H=2048 T=4096 (the largest token count of the page's validation
+sweep, "[TLERaw] Add NVSHMEM allreduce RMSNorm tutorial", FlagTree PR #1122,
+section Correctness: world size 4, hidden 2048, BF16, tokens 1 ... 4096).  A step
+is one arrms_fused call (rank sum, residual add, RMSNorm) on one batch of T rows.
+The metric is achieved HBM bandwidth: algorithmic bytes 2*T*H*(W+3) + 2*H (read W
+partials and the residual, write residual_out and norm_out, read the weight once)
+per call, divided by the time per call; also reported as a fraction of the 8 TB/s
+HBM3E peak, and as microseconds per call for T = 1, 16, 64, 128, 256, 1024, 4096.
+
+Inputs are resident in HBM before timing starts.  Calls walk through a 1.1 GiB
+pool of distinct input/output sets (more than twice the 256 MB Infinity Cache),
+so repeated calls cannot be served from cache.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "achieved HBM GB/s (% of peak) and µs/call, W=4 H=2048 at T=1..4096"
+SWEEP_T = [1, 16, 64, 128, 256, 1024, 4096]
+POOL_SLOTS = 10
+KERNEL_SRC = os.path.join(ROOT, "residual_add_rmsnorm_arrms_amd", "csrc", "arrms_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_w4_h2048_t4096.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(W, T, H):
+    return 2 * T * H * (W + 3) + 2 * H
+
+
+class Pool:
+    """POOL_SLOTS slots, each holding W partials, residual, residual_out and norm_out of
+    [T_max, H] BF16 in one device allocation.  A call with T rows uses rows
+    [j*T, (j+1)*T) of one slot, so successive calls touch fresh memory."""
+
+    def __init__(self, torch, x, res, w):
+        W, T, H = x.shape
+        self.W, self.T, self.H = W, T, H
+        dev = torch.device("cuda", 0)
+        self.tensor_elems = T * H
+        self.slot = torch.empty((POOL_SLOTS, W + 3, T, H), dtype=torch.bfloat16, device=dev)
+        self.slot[0, :W].copy_(x.to(dev))
+        self.slot[0, W].copy_(res.to(dev))
+        for s in range(1, POOL_SLOTS):
+            self.slot[s, :W + 1].copy_(self.slot[0, :W + 1])
+        self.weight = w.to(dev)
+        torch.cuda.synchronize()
+        self.base = self.slot.data_ptr()
+
+    @property
+    def nbytes(self):
+        return self.slot.numel() * 2
+
+    def sets(self, T):
+        """Pointer sets (partials, residual, residual_out, norm_out) for T-row calls."""
+        per_slot = self.T // T
+        out = []
+        for j in range(per_slot):
+            for s in range(POOL_SLOTS):
+                slot = self.base + s * (self.W + 3) * self.tensor_elems * 2
+                off = j * T * self.H * 2
+                t = lambda k: slot + k * self.tensor_elems * 2 + off
+                out.append(([t(r) for r in range(self.W)], t(self.W), t(self.W + 1), t(self.W + 2)))
+        return out
+
+
+class Caller:
+    """Pre-marshalled ctypes arguments, so the host side of a call costs little."""
+
+    def __init__(self, A, handle, sets, W, T, H, weight_ptr, eps, stream):
+        lib = A.load()
+        self.fn = lib.arrms_fused
+        vp = ctypes.c_void_p
+        self.args = []
+        for parts, res, ro, no in sets:
+            arr = (vp * W)(*parts)
+            self.args.append((vp(handle), arr, W, T, H, vp(res), vp(weight_ptr), ctypes.c_float(eps), vp(ro), vp(no)))
+        self.stream = vp(stream)
+        self.i = 0
+
+    def __call__(self):
+        a = self.args[self.i]
+        self.i = (self.i + 1) % len(self.args)
+        rc = self.fn(*a, self.stream)
+        if rc:
+            raise RuntimeError("arrms_fused returned %d" % rc)
+
+
+def time_back_to_back(torch, call, K):
+    """K calls between two synchronisations: (wall ms per call, GPU-event ms per call)."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(K):
+        call()
+    e1.record(s)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / K, e0.elapsed_time(e1) / K
+
+
+def time_per_launch(torch, call, K):
+    """Duration of each of K launches from an event pair around it, on the launch stream."""
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(s)
+        call()
+        b.record(s)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def time_isolated(torch, call, K):
+    """Each call alone: synchronise, event, call, event, synchronise (includes launch latency)."""
+    s = torch.cuda.current_stream()
+    out = []
+    for _ in range(K):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(s)
+        call()
+        b.record(s)
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    return out
+
+
+def time_graph(torch, call, calls_per_graph, replays):
+    """calls_per_graph calls captured in one HIP graph, replayed; ms per call."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        saved = call.stream
+        call.stream = ctypes.c_void_p(side.cuda_stream)
+        call()  # warm up on a side stream before capture
+        call.stream = saved
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    saved = call.stream
+    with torch.cuda.graph(g):
+        call.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for _ in range(calls_per_graph):
+            call()
+    call.stream = saved
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (replays * calls_per_graph)
+    del g
+    return ms
+
+
+def pct(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(q / 100.0 * (len(xs) - 1)))))]
+
+
+def copy_context(torch, nbytes):
+    """Plain device-to-device copy of nbytes (read nbytes + write nbytes): context, not the denominator."""
+    n = nbytes // 2
+    a = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return {"bytes_per_copy": 2 * n * 2, "ms": ms, "GB_s": 2 * n * 2 / (ms * 1e-3) / 1e9}
+
+
+def cpu_baseline(x, res, w, eps, budget_s):
+    """The oracle (single-threaded scalar C) on whole prefill calls, repeated up to budget_s."""
+    import oracle
+    import synth
+    xb, rb, wb = synth.bits(x), synth.bits(res), synth.bits(w)
+    W, T, H = xb.shape
+    times = []
+    t_start = time.perf_counter()
+    ref = None
+    while True:
+        t0 = time.perf_counter()
+        ref = oracle.fused(xb, rb, wb, eps)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= budget_s or len(times) >= 200:
+            break
+    med = statistics.median(times)
+    return ref, {
+        "value": algorithmic_bytes(W, T, H) / med / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "whole W=%d H=%d T=%d call (all rows), %d repetitions, median %.1f ms, single thread"
+                  % (W, H, T, len(times), med * 1e3),
+        "ms_per_call": med * 1e3,
+        "cpu": platform.processor() or platform.machine(),
+        "host_threads_available": os.cpu_count(),
+    }
+
+
+def traffic_record():
+    """FETCH_SIZE / WRITE_SIZE per launch measured by rocprofv3 for the current kernel source,
+    or None when the counters were taken on another version of the kernels."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--no-sweep", action="store_true", help="only the T=4096 headline")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the partial sums of all ranks are modelled as buffers already "
+              "in this GPU's memory, and nothing here uses a second GPU. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import residual_add_rmsnorm_arrms_amd as A
+    import synth
+
+    if not os.path.exists(A.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    wl = synth.WORKLOADS["prefill"]
+    W, T, H, eps = wl.world, wl.tokens, wl.hidden, wl.eps
+    log("generating inputs W=%d T=%d H=%d" % (W, T, H))
+    x, res, w = synth.make_inputs(wl)
+    pool = Pool(torch, x, res, w)
+    log("pool: %d slots, %.2f GiB" % (POOL_SLOTS, pool.nbytes / 2 ** 30))
+    op = A.FusedReduceResidualRMSNorm(max_world=W, max_tokens=T, max_hidden=H, device=0)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def caller(t):
+        return Caller(A, op.handle, pool.sets(t), W, t, H, pool.weight.data_ptr(), eps, stream)
+
+    # ---- headline: T=4096, K timed steps between synchronisations
+    call = caller(T)
+    plan = op.plan(pool.slot[0, :W], pool.slot[0, W], pool.weight, eps, pool.slot[0, W + 1], pool.slot[0, W + 2])
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    wall_ms, gpu_ms = time_back_to_back(torch, call, args.steps)
+    nbytes = algorithmic_bytes(W, T, H)
+    log("headline: %.3f us/call wall, %.3f us/call GPU events" % (wall_ms * 1e3, gpu_ms * 1e3))
+    # ---- roofline: kernel time from the events around the timed region (launch stream),
+    # i.e. gpu_ms per launch; per-launch event pairs give the spread (each pair adds
+    # the events' own overhead, about 2 us, so their mean is not used for the roofline)
+    achieved = nbytes / (gpu_ms * 1e-3) / 1e9
+    durs = time_per_launch(torch, call, max(200, min(args.steps, 2000)))
+    log("per-launch event pairs: p50 %.3f us, p90 %.3f, p99 %.3f; roofline %.1f GB/s" % (
+        pct(durs, 50) * 1e3, pct(durs, 90) * 1e3, pct(durs, 99) * 1e3, achieved))
+
+    # correctness of the timed configuration: one set against the oracle
+    torch.cuda.synchronize()
+    parity = None
+    cpu = None
+    if not args.no_cpu:
+        ref, cpu = cpu_baseline(x, res, w, eps, args.cpu_budget)
+        log("cpu oracle: %.2f GB/s (%s)" % (cpu["value"], cpu["sample"]))
+        s0 = pool.sets(T)[0]
+        import numpy as np
+        A.arrms_fused(op.handle, s0[0], W, T, H, s0[1], pool.weight.data_ptr(), eps, s0[2], s0[3], stream)
+        torch.cuda.synchronize()
+        ro = synth.bits(pool.slot[0, W + 1].cpu())
+        no = synth.bits(pool.slot[0, W + 2].cpu())
+        parity = {"residual_out_mismatches": int((ro != ref["residual_out"]).sum()),
+                  "norm_out_not_bit_identical": int((no != ref["norm_out"]).sum()),
+                  "elements": int(ro.size)}
+        log("parity of the timed configuration vs oracle: %s" % parity)
+
+    # ---- sweep over T: back-to-back, per-launch, isolated and graph replay
+    sweep = []
+    if not args.no_sweep:
+        for t in SWEEP_T:
+            c = caller(t)
+            p = op.plan(pool.slot[0, :W, :t], pool.slot[0, W, :t], pool.weight, eps, pool.slot[0, W + 1, :t],
+                        pool.slot[0, W + 2, :t])
+            for _ in range(100):
+                c()
+            k = 2000 if t <= 1024 else 1000
+            wall, gpu = time_back_to_back(torch, c, k)
+            d = time_per_launch(torch, c, 300)
+            iso = time_isolated(torch, c, 100)
+            gr = time_graph(torch, c, 100, 10)
+            b = algorithmic_bytes(W, t, H)
+            row = {"T": t, "variant": {1: "row", 2: "splith", 3: "scalar"}[p["variant"]], "grid": p["grid"],
+                   "block": p["block"], "bytes": b,
+                   "us_back_to_back_wall": wall * 1e3, "us_back_to_back_gpu": gpu * 1e3,
+                   "us_event_pair_p50": pct(d, 50) * 1e3, "us_event_pair_p90": pct(d, 90) * 1e3,
+                   "us_event_pair_p99": pct(d, 99) * 1e3,
+                   "us_isolated_p50": pct(iso, 50) * 1e3, "us_graph_replay": gr * 1e3,
+                   "GB_s_back_to_back": b / (gpu * 1e-3) / 1e9,
+                   "GB_s_graph": b / (gr * 1e-3) / 1e9}
+            row["frac_peak_back_to_back"] = row["GB_s_back_to_back"] / HBM_PEAK_GBS
+            sweep.append(row)
+            log("T=%5d %-6s b2b %.2f us (%.0f GB/s, %.1f%%), event pair p50 %.2f us, isolated %.2f us, "
+                "graph %.2f us" % (t, row["variant"], row["us_back_to_back_gpu"], row["GB_s_back_to_back"],
+                                   100 * row["frac_peak_back_to_back"], row["us_event_pair_p50"],
+                                   row["us_isolated_p50"], row["us_graph_replay"]))
+
+    copy = copy_context(torch, 512 * 2 ** 20)
+    log("copy context: %.1f GB/s" % copy["GB_s"])
+    tr = traffic_record()
+    op.close()
+
+    value = nbytes / (wall_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded SplitMix64/Box-Muller; x~N(0,0.5^2), residual~N(0,1), weight~U(0.5,1.5))",
+        "config": {"workload": "prefill: W=4 rank partials, T=4096 tokens, H=2048, BF16 in/out, eps=1e-6",
+                   "world": W, "tokens": T, "hidden": H, "io_dtype": "bf16", "accumulate": "f32 rank sum, f64 "
+                   "sum of squares", "algorithmic_bytes_per_call": nbytes, "plan": plan,
+                   "pool_bytes": pool.nbytes, "parallelism": "1 GPU"},
+        "frac_of_peak": value / HBM_PEAK_GBS,
+        "us_per_call": wall_ms * 1e3,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": (tr["fetch_bytes_per_launch"] + tr["write_bytes_per_launch"]) if tr else None,
+                     "kernel_mean_us": gpu_ms * 1e3, "launches_timed": args.steps,
+                     "timing": "HIP events on the launch stream around the K timed launches",
+                     "event_pair_p50_us": pct(durs, 50) * 1e3, "event_pair_p90_us": pct(durs, 90) * 1e3,
+                     "event_pair_p99_us": pct(durs, 99) * 1e3},
+        "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
+        "sweep": sweep,
+        "copy_context": copy,
+        "device": {"name": props.name, "compute_units": props.multi_processor_count,
+                   "gcn_arch": getattr(props, "gcnArchName", None), "memory_GiB": props.total_memory / 2 ** 30},
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    if tr:
+        out["roofline"]["traffic_detail"] = tr
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

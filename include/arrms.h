@@ -54,7 +54,7 @@ extern "C" {
 /* ---- kernel variants ----------------------------------------------------- */
 #define ARRMS_VARIANT_AUTO 0   /* choose per call from the shape (default) */
 #define ARRMS_VARIANT_ROW 1    /* one token row per workgroup (or per lane group) */
-#define ARRMS_VARIANT_SPLITH 2 /* each row split over several workgroups, two phases */
+#define ARRMS_VARIANT_SPLITH 2 /* each row split over several workgroups, two kernels */
 #define ARRMS_VARIANT_SCALAR 3 /* element-wise loads: any H, any 2-byte alignment */
 
 #define ARRMS_MAX_WORLD 16        /* largest W */
@@ -66,20 +66,25 @@ typedef struct arrms_ctx* arrms_handle_t;
 /* Launch plan of one call, as chosen by arrms_plan / arrms_query_plan. */
 typedef struct {
     int variant;         /* ARRMS_VARIANT_ROW, _SPLITH or _SCALAR (0 when tokens == 0) */
-    int grid;            /* workgroups launched (0: nothing is launched) */
+    int grid;            /* workgroups launched per kernel (0: nothing is launched) */
     int block;           /* threads per workgroup */
     int vec_per_thread;  /* 16-byte vectors per lane per input (row, split-H); 0 for scalar */
     int threads_per_row; /* lanes sharing one row (row) or one chunk (split-H) */
     int rows_per_block;  /* token rows per workgroup (row), else 1 */
     int chunks_per_row;  /* split-H chunks per row (split-H), else 1 */
+    int kernels;         /* kernel launches per call: 2 for split-H, else 1 (0: none) */
+    int blocks;          /* logical workgroups per kernel (grid minus padding of the XCD mapping) */
+    int xcd_chunk;       /* K > 0: runs of K consecutive workgroups (rows) kept on one XCD; 0: hardware order */
 } arrms_plan_t;
 
-/* Optional tuning overrides; 0 (or -1 where stated) keeps the automatic choice. */
+/* Optional tuning overrides; 0 (or -1 where stated) keeps the automatic choice.
+ * None of them changes any result bit, only speed. */
 typedef struct {
     int vec_per_thread;    /* row / split-H: 1, 2, 4 or 8 */
     int threads_per_row;   /* row: 16, 32 or a multiple of 64 up to 1024 */
     int splith_block;      /* split-H: threads per workgroup, 64..1024, multiple of 64 */
     int splith_max_tokens; /* automatic variant uses split-H when tokens <= this; -1 automatic */
+    int xcd_chunk;         /* -1 automatic; 0 hardware round-robin; K > 0 runs of K blocks per XCD */
 } arrms_tuning_t;
 
 /*
@@ -87,13 +92,13 @@ typedef struct {
  *   max_world  : largest W a call will pass, 1..ARRMS_MAX_WORLD
  *   max_tokens : largest T a call will pass, >= 0
  *   max_hidden : largest H a call will pass, 1..ARRMS_MAX_HIDDEN
- * Reads the device's compute-unit count, allocates and zeroes the split-H
- * workspace (max_tokens * ceil(max_hidden / 512) doubles plus max_tokens
- * 32-bit tickets), and reads the environment variable ARRMS_FORCE_VARIANT
- * (row | splith | scalar) once.  All one-time work happens here.
- * Returns ARRMS_OK and *out, or ARRMS_ERR_INVALID_ARG (bad limits, out NULL),
- * ARRMS_ERR_HIP (no such device) or ARRMS_ERR_OOM; *out is NULL on error.
- * Synchronous: the workspace is zeroed before it returns.
+ * Reads the device's compute-unit count, allocates the split-H workspace
+ * (max_tokens * ceil(max_hidden / 512) doubles, written before it is read in
+ * every call, so never cleared), and reads the environment variable
+ * ARRMS_FORCE_VARIANT (row | splith | scalar) once.  All one-time work
+ * happens here.  Returns ARRMS_OK and *out, or ARRMS_ERR_INVALID_ARG (bad
+ * limits, out NULL), ARRMS_ERR_HIP (no such device) or ARRMS_ERR_OOM; *out is
+ * NULL on error.
  */
 int arrms_create(arrms_handle_t* out, int device, int max_world, int max_tokens, int max_hidden);
 

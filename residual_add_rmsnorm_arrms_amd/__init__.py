@@ -45,7 +45,7 @@ EXPORTS = ("arrms_create", "arrms_fused", "arrms_destroy", "arrms_status_string"
 
 class arrms_plan_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("variant", "grid", "block", "vec_per_thread", "threads_per_row",
-                                            "rows_per_block", "chunks_per_row")]
+                                            "rows_per_block", "chunks_per_row", "kernels", "blocks", "xcd_chunk")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -53,7 +53,11 @@ class arrms_plan_t(ctypes.Structure):
 
 class arrms_tuning_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("vec_per_thread", "threads_per_row", "splith_block",
-                                            "splith_max_tokens")]
+                                            "splith_max_tokens", "xcd_chunk")]
+
+    @classmethod
+    def make(cls, vec_per_thread=0, threads_per_row=0, splith_block=0, splith_max_tokens=-1, xcd_chunk=-1):
+        return cls(vec_per_thread, threads_per_row, splith_block, splith_max_tokens, xcd_chunk)
 
 
 class ArrmsError(RuntimeError):
@@ -175,8 +179,7 @@ class FusedReduceResidualRMSNorm:
             raise ArrmsError(rc, "arrms_set_variant")
 
     def set_tuning(self, **kw) -> None:
-        t = arrms_tuning_t(kw.get("vec_per_thread", 0), kw.get("threads_per_row", 0), kw.get("splith_block", 0),
-                           kw.get("splith_max_tokens", -1)) if kw else None
+        t = arrms_tuning_t.make(**kw) if kw else None
         rc = arrms_set_tuning(self.handle, t)
         if rc != ARRMS_OK:
             raise ArrmsError(rc, "arrms_set_tuning")

@@ -29,7 +29,6 @@ struct arrms_ctx {
     arrms_tuning_t tuning;
     int ws_chunks;  // chunks per row the workspace holds
     double* ws;
-    unsigned* tickets;
     int last_hip_error;
 };
 
@@ -39,6 +38,10 @@ namespace {
 constexpr int kMinChunkVec = 64;
 // Largest (W + 2) * vectors-per-lane the row variant keeps in registers.
 constexpr int kMaxLiveVectors = 40;
+// Traffic of one automatic XCD run of the row variant.
+constexpr long kXcdRunBytes = 3L << 20;
+// Rows with less traffic than this never use split-H automatically.
+constexpr long kSplitMinRowBytes = 96L << 10;
 
 int chunks_capacity(int max_hidden) {
     const int nvec = (max_hidden + 7) / 8;
@@ -54,10 +57,11 @@ int row_max_threads(int world, int vpt) {
     return vpt == 1 ? 1024 : (vpt <= 4 ? 512 : 256);
 }
 
-int round_threads(int n) {
-    if (n <= 16) return 16;
-    if (n <= 32) return 32;
-    return (n + 63) / 64 * 64;
+// Smallest power of two >= n, at least 16 (16 and 32 are sub-wave row groups).
+int pow2_threads(int n) {
+    int t = 16;
+    while (t < n) t *= 2;
+    return t;
 }
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -75,29 +79,45 @@ bool valid_tuning(const arrms_tuning_t* t) {
     const int b = t->splith_block;
     if (!(b == 0 || (b > 0 && b % 64 == 0 && b <= 1024))) return false;
     if (t->splith_max_tokens < -1) return false;
+    if (t->xcd_chunk < -1) return false;
     return true;
+}
+
+// Launch shape of a vector-variant plan whose logical workgroup count is
+// p->blocks.  The XCD mapping keeps runs of K consecutive blocks on one XCD
+// (see logical_block in the kernels); K is clamped to blocks / 8 rounded up,
+// so the grid pads p->blocks by less than 8K.
+void finish_vector_plan(const arrms_tuning_t* t, arrms_plan_t* p, int auto_chunk) {
+    long k = (t && t->xcd_chunk >= 0) ? t->xcd_chunk : auto_chunk;
+    const long whole = (p->blocks + 7L) / 8;
+    if (k > whole) k = whole;
+    const long grid = k ? (p->blocks + 8 * k - 1) / (8 * k) * (8 * k) : p->blocks;
+    if (grid > 0x7fffffffL) k = 0;  // keep the launch within the grid-size limit
+    p->xcd_chunk = static_cast<int>(k);
+    p->grid = k ? static_cast<int>(grid) : p->blocks;
 }
 
 // Row variant plan; returns ARRMS_ERR_UNSUPPORTED when the shape or the
 // tuning overrides do not fit the row kernels.
+//
+// Automatic lane layout (measured on MI355X, W=4 H=2048, W=8 H=5120 and
+// H=8192): row groups of a power-of-two lane count do better than exact fits
+// (a 5-wave group for H=5120 loses about 4% to an 8-wave group with idle
+// lanes), and the best groups hold 256 to 512 lanes.  So: the fewest vectors
+// per lane whose power-of-two row group is at most 512 lanes.
 int plan_row(int world, int tokens, int hidden, const arrms_tuning_t* t, arrms_plan_t* p) {
     const int nvec = hidden / 8;
     const int we = world_extent(world);
     int best_vpt = 0, best_tpr = 0;
-    long best_waste = 0;
     for (int vpt = 1; vpt <= 8; vpt *= 2) {
         if (t && t->vec_per_thread && t->vec_per_thread != vpt) continue;
         if ((we + 2) * vpt > kMaxLiveVectors) continue;
-        int tpr = round_threads((nvec + vpt - 1) / vpt);
+        int tpr = pow2_threads((nvec + vpt - 1) / vpt);
         if (t && t->threads_per_row) tpr = t->threads_per_row;
         if (tpr > row_max_threads(world, vpt) || static_cast<long>(tpr) * vpt < nvec) continue;
-        const long waste = static_cast<long>(tpr) * vpt - nvec;
-        // least idle vector slots, then the row group closest to 256 lanes
-        if (!best_vpt || waste < best_waste ||
-            (waste == best_waste && abs(tpr - 256) < abs(best_tpr - 256))) {
+        if (!best_vpt || (best_tpr > 512 && tpr < best_tpr)) {
             best_vpt = vpt;
             best_tpr = tpr;
-            best_waste = waste;
         }
     }
     if (!best_vpt) return ARRMS_ERR_UNSUPPORTED;
@@ -109,7 +129,18 @@ int plan_row(int world, int tokens, int hidden, const arrms_tuning_t* t, arrms_p
     p->rows_per_block = rpb;
     p->chunks_per_row = 1;
     p->block = best_tpr * rpb;
-    p->grid = (tokens + rpb - 1) / rpb;
+    p->blocks = (tokens + rpb - 1) / rpb;
+    p->kernels = 1;
+    // Automatic XCD runs: about 3 MiB of traffic per run, a power of two of
+    // blocks (measured best: 64 blocks at W=4 H=2048, 16 at W=8 H=5120/8192);
+    // small grids keep the hardware order.
+    int k = 0;
+    if (p->blocks >= 64) {
+        const long block_bytes = 2L * rpb * (world + 3) * hidden;
+        k = 1;
+        while (2L * k * block_bytes <= kXcdRunBytes) k *= 2;
+    }
+    finish_vector_plan(t, p, k);
     return ARRMS_OK;
 }
 
@@ -146,14 +177,16 @@ int plan_splith(int cu_count, int max_hidden, int world, int tokens, int hidden,
     const int chunk_vec = block * vpt;
     const int chunks = (nvec + chunk_vec - 1) / chunk_vec;
     if (chunks > cap) return ARRMS_ERR_UNSUPPORTED;
-    if (static_cast<long>(tokens) * chunks > 0x7fffffffL) return ARRMS_ERR_UNSUPPORTED;
+    if (static_cast<long>(tokens) * chunks > 0x7ffffff0L) return ARRMS_ERR_UNSUPPORTED;
     p->variant = ARRMS_VARIANT_SPLITH;
     p->vec_per_thread = vpt;
     p->threads_per_row = block;
     p->rows_per_block = 1;
     p->chunks_per_row = chunks;
     p->block = block;
-    p->grid = tokens * chunks;
+    p->blocks = tokens * chunks;
+    p->kernels = 2;
+    finish_vector_plan(t, p, 0);
     return ARRMS_OK;
 }
 
@@ -166,13 +199,21 @@ void plan_scalar(int tokens, int hidden, arrms_plan_t* p) {
     p->rows_per_block = 1;
     p->chunks_per_row = 1;
     p->block = block;
+    p->blocks = tokens;
     p->grid = tokens;
+    p->kernels = 1;
+    p->xcd_chunk = 0;
 }
 
-// Automatic crossover to split-H: rows that leave most compute units idle.
-int auto_splith_max_tokens(int cu_count, int hidden) {
-    (void)hidden;
-    return cu_count / 8;
+// Automatic crossover to split-H, measured on MI355X with HIP-graph replay
+// (GPU time per call): rows of up to 28 KiB of traffic (W=4 H=2048) are
+// faster with the one-kernel row variant at every T; rows of 110-224 KiB
+// (W=8 H=5120 / H=8192, W=4 H=16384) are faster split over several
+// workgroups while T stays below about 64 rows per 96 KiB of row traffic.
+int auto_splith_max_tokens(int cu_count, int world, int hidden) {
+    const long row_bytes = 2L * (world + 3) * hidden;
+    if (row_bytes < kSplitMinRowBytes) return 0;
+    return static_cast<int>((cu_count / 4) * row_bytes / kSplitMinRowBytes);
 }
 
 }  // namespace
@@ -247,7 +288,7 @@ int arrms_plan(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
         return ARRMS_OK;
     }
     int split_max = (tuning && tuning->splith_max_tokens >= 0) ? tuning->splith_max_tokens
-                                                              : auto_splith_max_tokens(cu_count, hidden);
+                                                              : auto_splith_max_tokens(cu_count, world, hidden);
     if (hidden > ARRMS_ROW_MAX_HIDDEN || tokens <= split_max) {
         const int rc = plan_splith(cu_count, max_hidden, world, tokens, hidden, tuning, plan);
         if (rc == ARRMS_OK || hidden > ARRMS_ROW_MAX_HIDDEN) return rc;
@@ -299,14 +340,10 @@ int arrms_create(arrms_handle_t* out, int device, int max_world, int max_tokens,
     }
     int rc = ARRMS_OK;
     const size_t rows = max_tokens > 0 ? static_cast<size_t>(max_tokens) : 1;
-    hipError_t e = hipMalloc(reinterpret_cast<void**>(&h->ws), rows * h->ws_chunks * sizeof(double));
-    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&h->tickets), rows * sizeof(unsigned));
-    if (e == hipSuccess) e = hipMemset(h->tickets, 0, rows * sizeof(unsigned));
-    if (e == hipSuccess) e = hipDeviceSynchronize();
+    const hipError_t e = hipMalloc(reinterpret_cast<void**>(&h->ws), rows * h->ws_chunks * sizeof(double));
     if (e != hipSuccess) rc = (e == hipErrorOutOfMemory) ? ARRMS_ERR_OOM : ARRMS_ERR_HIP;
     if (rc != ARRMS_OK) {
         if (h->ws) (void)hipFree(h->ws);
-        if (h->tickets) (void)hipFree(h->tickets);
         delete h;
         h = nullptr;
     }
@@ -322,7 +359,6 @@ int arrms_destroy(arrms_handle_t h) {
     (void)hipSetDevice(h->device);
     int rc = ARRMS_OK;
     if (h->ws && hipFree(h->ws) != hipSuccess) rc = ARRMS_ERR_HIP;
-    if (h->tickets && hipFree(h->tickets) != hipSuccess) rc = ARRMS_ERR_HIP;
     if (prev >= 0 && prev != h->device) (void)hipSetDevice(prev);
     delete h;
     return rc;
@@ -371,7 +407,6 @@ int arrms_fused(arrms_handle_t h, const void* const* partials, int world, int to
     a.residual_out = residual_out;
     a.norm_out = norm_out;
     a.ws = h->ws;
-    a.tickets = h->tickets;
     a.hidden_d = static_cast<double>(hidden);
     a.eps = eps;
     a.world = world;
@@ -382,6 +417,8 @@ int arrms_fused(arrms_handle_t h, const void* const* partials, int world, int to
     a.rows_per_block = p.rows_per_block;
     a.chunks = p.chunks_per_row;
     a.chunk_vec = p.block * p.vec_per_thread;
+    a.blocks = p.blocks;
+    a.xcd_chunk = p.xcd_chunk;
 
     int prev = -1;
     if (hipGetDevice(&prev) != hipSuccess) prev = -1;

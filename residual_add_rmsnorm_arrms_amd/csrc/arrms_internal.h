@@ -24,7 +24,6 @@ struct Args {
     void* residual_out;     // BF16 [tokens][hidden]; may equal residual
     void* norm_out;         // BF16 [tokens][hidden]
     double* ws;             // split-H: [tokens][chunks] binary64 partial sums of squares
-    unsigned* tickets;      // split-H: [tokens] arrival counters, zero between calls
     double hidden_d;        // H as binary64 (the divisor of the mean of squares)
     float eps;
     int world;              // W
@@ -35,10 +34,13 @@ struct Args {
     int rows_per_block;     // row: rows per workgroup
     int chunks;             // split-H: chunks per row
     int chunk_vec;          // split-H: vectors per chunk
+    int blocks;             // logical workgroups (the launched grid may add XCD padding)
+    int xcd_chunk;          // K > 0: runs of K consecutive blocks per XCD (grid a multiple of 8K)
 };
 
 // Each launcher returns the hipError_t of the launch itself.
 hipError_t launch_row(const Args& a, int vec_per_thread, int grid, int block, hipStream_t s);
+// Split-H launches two kernels on `s`: the partial pass, then the norm pass.
 hipError_t launch_splith(const Args& a, int vec_per_thread, int grid, int block, hipStream_t s);
 hipError_t launch_scalar(const Args& a, int grid, int block, hipStream_t s);
 

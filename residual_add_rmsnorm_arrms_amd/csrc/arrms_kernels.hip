@@ -54,10 +54,37 @@ __device__ __forceinline__ uint32_t pack2(uint32_t lo_rounded, uint32_t hi_round
     return (lo_rounded >> 16) | hi_rounded;
 }
 
+// 16-byte loads and stores.  The partials and the residual are read exactly
+// once, so they are loaded with the non-temporal (streaming) hint; the weight,
+// read by every row, is loaded normally so that it stays cached.  The outputs
+// are written once and not read again by this kernel: streaming stores.
 __device__ __forceinline__ u32x4 ld4(const void* base, size_t i) {
     return static_cast<const u32x4*>(base)[i];
 }
+__device__ __forceinline__ u32x4 ld4_stream(const void* base, size_t i) {
+    return __builtin_nontemporal_load(static_cast<const u32x4*>(base) + i);
+}
 __device__ __forceinline__ void st4(void* base, size_t i, u32x4 v) { static_cast<u32x4*>(base)[i] = v; }
+__device__ __forceinline__ void st4_stream(void* base, size_t i, u32x4 v) {
+    __builtin_nontemporal_store(v, static_cast<u32x4*>(base) + i);
+}
+
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8).  With xcd_chunk = K > 0 the launched grid is a multiple of 8K and
+// the i-th workgroup an XCD receives takes logical block (8 * (i / K) + x) * K
+// + i % K (x = its XCD): runs of K consecutive blocks (rows) stay on one XCD,
+// and at any moment the 8 XCDs work on neighbouring runs.  K = 0 keeps the
+// hardware's round-robin order.  Returns -1 for padding blocks past a.blocks.
+__device__ __forceinline__ int logical_block(const Args& a) {
+    const int b = blockIdx.x;
+    const int k = a.xcd_chunk;
+    if (k == 0) return b;
+    const int x = b & 7;
+    const int i = b >> 3;
+    const int j = i / k;
+    const int l = (j * 8 + x) * k + (i - j * k);
+    return l < a.blocks ? l : -1;
+}
 
 // ---------------------------------------------------------------- reductions
 template <int CTRL>
@@ -173,10 +200,12 @@ __global__ void __launch_bounds__((row_max_threads<W, VPT>())) row_kernel(const 
     constexpr int WA = W > 0 ? W : kMaxWorld;
     const int world = W > 0 ? W : a.world;
     const int tpr = a.threads_per_row;
+    const int block = logical_block(a);
+    if (block < 0) return;  // padding workgroup of the XCD mapping (whole workgroup)
     const int tid = threadIdx.x;
     const int row_in_block = tid / tpr;
     const int lane = tid - row_in_block * tpr;
-    const int row = blockIdx.x * a.rows_per_block + row_in_block;
+    const int row = block * a.rows_per_block + row_in_block;
     const bool row_ok = row < a.tokens;
     const size_t base = static_cast<size_t>(row_ok ? row : 0) * static_cast<size_t>(a.nvec);
 
@@ -191,8 +220,8 @@ __global__ void __launch_bounds__((row_max_threads<W, VPT>())) row_kernel(const 
         if (ok[k]) {
 #pragma unroll
             for (int r = 0; r < WA; ++r)
-                if (W > 0 || r < world) xv[k][r] = ld4(a.x.p[r], base + v);
-            rv[k] = ld4(a.residual, base + v);
+                if (W > 0 || r < world) xv[k][r] = ld4_stream(a.x.p[r], base + v);
+            rv[k] = ld4_stream(a.residual, base + v);
             wv[k] = ld4(a.weight, v);
         }
     }
@@ -203,7 +232,7 @@ __global__ void __launch_bounds__((row_max_threads<W, VPT>())) row_kernel(const 
     for (int k = 0; k < VPT; ++k) {
         if (ok[k]) {
             ro[k] = residual_vec<W>(xv[k], world, rv[k], ss);
-            st4(a.residual_out, base + lane + k * tpr, ro[k]);
+            st4_stream(a.residual_out, base + lane + k * tpr, ro[k]);
         }
     }
 
@@ -223,28 +252,32 @@ __global__ void __launch_bounds__((row_max_threads<W, VPT>())) row_kernel(const 
 
 #pragma unroll
     for (int k = 0; k < VPT; ++k)
-        if (ok[k]) st4(a.norm_out, base + lane + k * tpr, norm_vec(ro[k], inv, wv[k]));
+        if (ok[k]) st4_stream(a.norm_out, base + lane + k * tpr, norm_vec(ro[k], inv, wv[k]));
 }
 
 // ------------------------------------------------------------ split-H variant
-// For few rows: row t is cut into `chunks` chunks of chunk_vec vectors, one
-// workgroup each (grid = tokens * chunks).  Phase 1 (every workgroup): rank
-// sum, residual add and residual_out store for its chunk, then the chunk's
-// binary64 sum of squares goes to ws[t][chunk].  The workgroup then releases
-// its stores (device-scope fence) and takes a ticket on the row's counter.
-// Phase 2 (only the workgroup that draws the last ticket, so no workgroup ever
-// waits for another): acquire, add ws[t][0..chunks-1] in chunk order, compute
-// 1/RMS, re-read the row's residual_out and write norm_out, then reset the
-// counter to zero for the next call.
+// For few rows: row t is cut into `chunks` chunks of chunk_vec vectors and each
+// chunk gets a workgroup, in two kernels launched back to back on the stream.
+// Phase 1: rank sum, residual add and residual_out store for the chunk; the
+// chunk's binary64 sum of squares goes to ws[t][chunk].  Phase 2: each chunk's
+// workgroup adds ws[t][0..chunks-1] in chunk order (every workgroup of a row
+// gets the same bits), computes 1/RMS, re-reads its residual_out chunk and
+// writes norm_out.  The kernel boundary orders phase 1's stores before phase
+// 2's loads on every XCD; a single-kernel hand-off between workgroups would
+// need a device-scope release per workgroup, which writes back the XCD's whole
+// L2 and costs far more than the second launch.  No workgroup ever waits for
+// another, and the workspace needs no reset between calls.
 template <int W>
 constexpr int splith_max_threads() { return (W == 0 || W > 8) ? 512 : 1024; }
 
 template <int W, int VPT>
-__global__ void __launch_bounds__(splith_max_threads<W>()) splith_kernel(const Args a) {
+__global__ void __launch_bounds__(splith_max_threads<W>()) splith_partial_kernel(const Args a) {
     constexpr int WA = W > 0 ? W : kMaxWorld;
     const int world = W > 0 ? W : a.world;
-    const int row = blockIdx.x / a.chunks;
-    const int chunk = blockIdx.x - row * a.chunks;
+    const int block = logical_block(a);
+    if (block < 0) return;
+    const int row = block / a.chunks;
+    const int chunk = block - row * a.chunks;
     const int tid = threadIdx.x;
     const int nthreads = blockDim.x;
     const int v0 = chunk * a.chunk_vec;
@@ -261,8 +294,8 @@ __global__ void __launch_bounds__(splith_max_threads<W>()) splith_kernel(const A
         if (ok[k]) {
 #pragma unroll
             for (int r = 0; r < WA; ++r)
-                if (W > 0 || r < world) xv[k][r] = ld4(a.x.p[r], base + v);
-            rv[k] = ld4(a.residual, base + v);
+                if (W > 0 || r < world) xv[k][r] = ld4_stream(a.x.p[r], base + v);
+            rv[k] = ld4_stream(a.residual, base + v);
         }
     }
     double ss = 0.0;
@@ -270,42 +303,36 @@ __global__ void __launch_bounds__(splith_max_threads<W>()) splith_kernel(const A
     for (int k = 0; k < VPT; ++k) {
         if (ok[k]) {
             const u32x4 ro = residual_vec<W>(xv[k], world, rv[k], ss);
-            st4(a.residual_out, base + v0 + tid + k * nthreads, ro);
+            st4(a.residual_out, base + v0 + tid + k * nthreads, ro);  // re-read by phase 2: keep cached
         }
     }
 
     __shared__ double wave_ss[16];
-    __shared__ int is_last;
     ss = seg_sum(ss, 64);
     if ((tid & 63) == 0) wave_ss[tid >> 6] = ss;
     __syncthreads();
     if (tid == 0) {
         double t = wave_ss[0];
         for (int i = 1; i < (nthreads >> 6); ++i) t = t + wave_ss[i];
-        __hip_atomic_store(&a.ws[static_cast<size_t>(row) * a.chunks + chunk], t, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        a.ws[static_cast<size_t>(row) * a.chunks + chunk] = t;
     }
-    // Release this workgroup's residual_out chunk and partial sum to the device.
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(&a.tickets[row], 1u, __ATOMIC_ACQ_REL,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        is_last = prev == static_cast<unsigned>(a.chunks - 1);
-    }
-    __syncthreads();
-    if (!is_last) return;
-    // Acquire the other workgroups' stores before reading them.
-    __threadfence();
+}
 
-    double total = 0.0;
-    for (int c = 0; c < a.chunks; ++c)
-        total = total + __hip_atomic_load(&a.ws[static_cast<size_t>(row) * a.chunks + c], __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
+__global__ void __launch_bounds__(1024) splith_norm_kernel(const Args a) {
+    const int block = logical_block(a);
+    if (block < 0) return;
+    const int row = block / a.chunks;
+    const int chunk = block - row * a.chunks;
+    const int tid = threadIdx.x;
+    const int v0 = chunk * a.chunk_vec;
+    const int v1 = min(a.nvec, v0 + a.chunk_vec);
+    const size_t base = static_cast<size_t>(row) * static_cast<size_t>(a.nvec);
+    const double* part = a.ws + static_cast<size_t>(row) * a.chunks;
+    double total = part[0];
+    for (int c = 1; c < a.chunks; ++c) total = total + part[c];
     const float inv = inv_rms(total, a.hidden_d, a.eps);
-    for (int v = tid; v < a.nvec; v += nthreads)
-        st4(a.norm_out, base + v, norm_vec(ld4(a.residual_out, base + v), inv, ld4(a.weight, v)));
-    if (tid == 0) __hip_atomic_store(&a.tickets[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int v = v0 + tid; v < v1; v += blockDim.x)
+        st4_stream(a.norm_out, base + v, norm_vec(ld4(a.residual_out, base + v), inv, ld4(a.weight, v)));
 }
 
 // -------------------------------------------------------------- scalar variant
@@ -382,19 +409,19 @@ const void* row_fn(int world) {
 template <int VPT>
 const void* splith_fn(int world) {
     switch (world) {
-        case 1: return reinterpret_cast<const void*>(&splith_kernel<1, VPT>);
-        case 2: return reinterpret_cast<const void*>(&splith_kernel<2, VPT>);
-        case 3: return reinterpret_cast<const void*>(&splith_kernel<3, VPT>);
-        case 4: return reinterpret_cast<const void*>(&splith_kernel<4, VPT>);
-        case 5: return reinterpret_cast<const void*>(&splith_kernel<5, VPT>);
-        case 6: return reinterpret_cast<const void*>(&splith_kernel<6, VPT>);
-        case 7: return reinterpret_cast<const void*>(&splith_kernel<7, VPT>);
-        case 8: return reinterpret_cast<const void*>(&splith_kernel<8, VPT>);
+        case 1: return reinterpret_cast<const void*>(&splith_partial_kernel<1, VPT>);
+        case 2: return reinterpret_cast<const void*>(&splith_partial_kernel<2, VPT>);
+        case 3: return reinterpret_cast<const void*>(&splith_partial_kernel<3, VPT>);
+        case 4: return reinterpret_cast<const void*>(&splith_partial_kernel<4, VPT>);
+        case 5: return reinterpret_cast<const void*>(&splith_partial_kernel<5, VPT>);
+        case 6: return reinterpret_cast<const void*>(&splith_partial_kernel<6, VPT>);
+        case 7: return reinterpret_cast<const void*>(&splith_partial_kernel<7, VPT>);
+        case 8: return reinterpret_cast<const void*>(&splith_partial_kernel<8, VPT>);
         default: break;
     }
     if constexpr (VPT == 1) {
-        if (world == 16) return reinterpret_cast<const void*>(&splith_kernel<16, 1>);
-        return reinterpret_cast<const void*>(&splith_kernel<0, 1>);
+        if (world == 16) return reinterpret_cast<const void*>(&splith_partial_kernel<16, 1>);
+        return reinterpret_cast<const void*>(&splith_partial_kernel<0, 1>);
     }
     return nullptr;
 }
@@ -422,7 +449,9 @@ hipError_t launch_splith(const Args& a, int vpt, int grid, int block, hipStream_
         default: return hipErrorInvalidValue;
     }
     if (!fn) return hipErrorInvalidValue;
-    return launch(fn, a, grid, block, s);
+    const hipError_t e = launch(fn, a, grid, block, s);
+    if (e != hipSuccess) return e;
+    return launch(reinterpret_cast<const void*>(&splith_norm_kernel), a, grid, block, s);
 }
 
 hipError_t launch_scalar(const Args& a, int grid, int block, hipStream_t s) {

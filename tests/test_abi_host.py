@@ -54,6 +54,11 @@ def bufs(W, T, H, align=256, off=0):
                 norm_out=ptrs[W + 3])
 
 
+def grid_of(p):
+    k = p["xcd_chunk"]
+    return -(-p["blocks"] // (8 * k)) * (8 * k) if k else p["blocks"]
+
+
 def plan(W, T, H, variant=A.ARRMS_VARIANT_AUTO, tuning=None, eps=1e-6, cu=CU, lim=LIM, **over):
     b = bufs(W, T, H)
     b.update(over)
@@ -66,8 +71,9 @@ def test_prefill_shape_uses_row_variant():
     assert rc == A.ARRMS_OK
     assert p["variant"] == A.ARRMS_VARIANT_ROW
     assert p["threads_per_row"] * p["vec_per_thread"] >= 2048 // 8
-    assert p["grid"] * p["rows_per_block"] >= 4096
+    assert p["blocks"] * p["rows_per_block"] >= 4096
     assert p["block"] % 64 == 0 and p["block"] <= 1024
+    assert p["kernels"] == 1 and p["grid"] == grid_of(p)
 
 
 @pytest.mark.parametrize("W,T,H", [(8, 8192, 8192), (8, 16383, 5120), (2, 4, 128), (4, 1000, 64), (1, 5, 8),
@@ -77,7 +83,8 @@ def test_row_plans_cover_the_row(W, T, H):
     assert rc == A.ARRMS_OK, (W, T, H)
     nvec = H // 8
     assert p["threads_per_row"] * p["vec_per_thread"] >= nvec
-    assert p["grid"] * p["rows_per_block"] >= T > (p["grid"] - 1) * p["rows_per_block"]
+    assert p["blocks"] * p["rows_per_block"] >= T > (p["blocks"] - 1) * p["rows_per_block"]
+    assert p["grid"] == grid_of(p)
     assert p["block"] == p["threads_per_row"] * p["rows_per_block"] and p["block"] % 64 == 0
     assert p["threads_per_row"] in (16, 32) or p["threads_per_row"] % 64 == 0
     we = W if (W <= 8 or W == 16) else 16
@@ -92,12 +99,13 @@ def test_splith_plans(W, T, H):
     chunk = p["block"] * p["vec_per_thread"]
     assert p["chunks_per_row"] == -(-(H // 8) // chunk)
     assert p["chunks_per_row"] <= -(-(65536 // 8) // 64)
-    assert p["grid"] == T * p["chunks_per_row"]
+    assert p["blocks"] == T * p["chunks_per_row"] and p["kernels"] == 2
+    assert p["grid"] == grid_of(p)
     assert p["block"] % 64 == 0 and p["block"] <= (512 if W > 8 else 1024)
 
 
 def test_auto_selection():
-    assert plan(4, 1, 2048)[1]["variant"] == A.ARRMS_VARIANT_SPLITH      # decode: few rows
+    assert plan(4, 1, 2048)[1]["variant"] == A.ARRMS_VARIANT_ROW         # decode: one kernel is faster
     assert plan(4, 4096, 2048)[1]["variant"] == A.ARRMS_VARIANT_ROW      # prefill
     assert plan(4, 4096, 32768)[1]["variant"] == A.ARRMS_VARIANT_SPLITH  # H beyond the row kernels
     assert plan(4, 100, 1000)[1]["variant"] == A.ARRMS_VARIANT_ROW       # H % 8 == 0
@@ -105,8 +113,39 @@ def test_auto_selection():
     b = bufs(4, 100, 2048)
     rc, p = plan(4, 100, 2048, residual=b["residual"] + 2)               # 2-byte aligned only
     assert rc == A.ARRMS_OK and p["variant"] == A.ARRMS_VARIANT_SCALAR
-    t = A.arrms_tuning_t(0, 0, 0, 0)
-    assert plan(4, 1, 2048, tuning=t)[1]["variant"] == A.ARRMS_VARIANT_ROW  # crossover forced to 0
+    t = A.arrms_tuning_t.make(splith_max_tokens=8)
+    assert plan(4, 8, 2048, tuning=t)[1]["variant"] == A.ARRMS_VARIANT_SPLITH  # crossover moved up
+    assert plan(4, 9, 2048, tuning=t)[1]["variant"] == A.ARRMS_VARIANT_ROW
+
+
+def test_xcd_mapping_plans():
+    rc, p = plan(4, 4096, 2048, tuning=A.arrms_tuning_t.make(xcd_chunk=0))
+    assert rc == A.ARRMS_OK and p["xcd_chunk"] == 0 and p["grid"] == p["blocks"]
+    rc, p = plan(4, 3, 2048, tuning=A.arrms_tuning_t.make(xcd_chunk=1))
+    assert p["xcd_chunk"] == 1 and p["grid"] == 8 and p["blocks"] == 3
+    rc, p = plan(4, 1000, 2048, tuning=A.arrms_tuning_t.make(xcd_chunk=16))
+    assert p["xcd_chunk"] == 16 and p["grid"] == 1024 and p["blocks"] == 1000
+    rc, p = plan(4, 1000, 2048, tuning=A.arrms_tuning_t.make(xcd_chunk=10 ** 6))  # clamped to blocks / 8
+    assert p["xcd_chunk"] == 125 and p["grid"] == 1000
+    rc, p = plan(4, 3, 2048)
+    assert p["xcd_chunk"] == 0 and p["grid"] == 3                       # small grids: no padding
+    rc, p = plan(4, 100, 1001)
+    assert p["variant"] == A.ARRMS_VARIANT_SCALAR and p["xcd_chunk"] == 0 and p["grid"] == 100
+
+
+@pytest.mark.parametrize("blocks,k", [(8, 1), (13, 1), (100, 3), (64, 8), (1000, 16), (4096, 512), (77, 10)])
+def test_xcd_mapping_is_a_bijection(blocks, k):
+    """The kernels' logical-block formula, run on the host over the planned grid: every
+    logical block exactly once, padding workgroups only past the end."""
+    grid = -(-blocks // (8 * k)) * (8 * k)
+    seen = []
+    for b in range(grid):
+        x, i = b % 8, b // 8
+        j = i // k
+        l = (j * 8 + x) * k + (i - j * k)
+        if l < blocks:
+            seen.append(l)
+    assert sorted(seen) == list(range(blocks))
 
 
 def test_forced_variant_unsupported():
@@ -114,7 +153,7 @@ def test_forced_variant_unsupported():
     assert plan(4, 10, 1001, variant=A.ARRMS_VARIANT_SPLITH)[0] == A.ARRMS_ERR_UNSUPPORTED
     assert plan(4, 10, 32768, variant=A.ARRMS_VARIANT_ROW)[0] == A.ARRMS_ERR_UNSUPPORTED
     assert plan(4, 10, 1001, variant=A.ARRMS_VARIANT_SCALAR)[0] == A.ARRMS_OK
-    t = A.arrms_tuning_t(8, 0, 0, -1)
+    t = A.arrms_tuning_t.make(vec_per_thread=8)
     assert plan(8, 10, 2048, variant=A.ARRMS_VARIANT_ROW, tuning=t)[0] == A.ARRMS_ERR_UNSUPPORTED  # registers
 
 
@@ -170,7 +209,8 @@ def test_aliasing_rules():
     assert plan(4, 16, 2048, partials=[p[0], p[0], p[0], p[0]])[0] == A.ARRMS_OK
 
 
-@pytest.mark.parametrize("t", [(3, 0, 0, -1), (0, 48, 0, -1), (0, 2048, 0, -1), (0, 0, 100, -1), (0, 0, 0, -2)])
+@pytest.mark.parametrize("t", [(3, 0, 0, -1, -1), (0, 48, 0, -1, -1), (0, 2048, 0, -1, -1),
+                               (0, 0, 100, -1, -1), (0, 0, 0, -2, -1), (0, 0, 0, -1, -2)])
 def test_invalid_tuning(t):
     assert plan(4, 16, 2048, tuning=A.arrms_tuning_t(*t))[0] == A.ARRMS_ERR_INVALID_ARG
 
@@ -193,3 +233,19 @@ def test_create_rejects_bad_limits():
                  (-1, 4, 16, 2048)]:
         rc, h = A.arrms_create(*args)
         assert rc == A.ARRMS_ERR_INVALID_ARG and h is None
+
+
+@pytest.mark.parametrize("W,T,H,variant,vpt,tpr,k", [
+    (4, 4096, 2048, A.ARRMS_VARIANT_ROW, 1, 256, 64),      # prefill: 256-lane rows, 64-row XCD runs
+    (8, 8192, 8192, A.ARRMS_VARIANT_ROW, 2, 512, 16),
+    (8, 16383, 5120, A.ARRMS_VARIANT_ROW, 2, 512, 16),     # 8-wave rows beat exact 5-wave rows
+    (4, 16, 2048, A.ARRMS_VARIANT_ROW, 1, 256, 0),         # decode, small rows: one kernel
+    (8, 1, 8192, A.ARRMS_VARIANT_SPLITH, 1, 64, 0),        # decode, large rows: split over CUs
+    (8, 128, 8192, A.ARRMS_VARIANT_ROW, 2, 512, 16),
+])
+def test_measured_automatic_choices(W, T, H, variant, vpt, tpr, k):
+    """The automatic choices the MI355X measurements led to (speed only; results are
+    identical in every variant and layout)."""
+    rc, p = plan(W, T, H)
+    assert rc == A.ARRMS_OK
+    assert (p["variant"], p["vec_per_thread"], p["threads_per_row"], p["xcd_chunk"]) == (variant, vpt, tpr, k)

@@ -128,6 +128,20 @@ def test_splith_tuning_grid(W, H, block, vpt):
     assert plan["block"] == block and plan["vec_per_thread"] == vpt
 
 
+XCD_CASES = [(W, T, H, variant, xcd) for W, T, H in [(4, 4096, 2048), (8, 77, 5120), (4, 3, 2048)]
+             for variant in (ROW, SPLITH) for xcd in (0, 1, 7, 64, 10 ** 6)]
+
+
+@pytest.mark.parametrize("W,T,H,variant,xcd", XCD_CASES)
+def test_xcd_mapping(W, T, H, variant, xcd):
+    """The XCD block mapping (with its padding workgroups) changes no result bit."""
+    plan, _ = parity(W, T, H, variant=variant, tuning=dict(xcd_chunk=xcd), seed=21 + T)
+    k = plan["xcd_chunk"]
+    assert k == min(xcd, -(-plan["blocks"] // 8))
+    if k:
+        assert plan["grid"] % (8 * k) == 0 and 0 <= plan["grid"] - plan["blocks"] < 8 * k
+
+
 # ------------------------------------------------------------ semantics and edge cases
 @pytest.mark.parametrize("variant", [ROW, SPLITH, SCALAR])
 def test_in_place_residual(variant):
@@ -193,9 +207,9 @@ def test_deterministic(variant, T):
         assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
 
 
-def test_splith_back_to_back_calls_reset_tickets():
-    """Many split-H calls in a row on one handle and stream, each on different data: the
-    arrival counters must return to zero after every call."""
+def test_splith_back_to_back_calls_share_workspace():
+    """Many split-H calls in a row on one handle and stream, each on different data and
+    row counts, all through the handle's one workspace."""
     say("case split-H back-to-back")
     dev = torch.device("cuda", 0)
     o = op()
