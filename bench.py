@@ -43,7 +43,13 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the kernel source without comments and blank lines: what the counters were
+    measured on (a comment edit leaves it unchanged, a code edit does not)."""
+    import re
+    text = open(KERNEL_SRC).read()
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def algorithmic_bytes(W, T, H):
@@ -208,6 +214,16 @@ def copy_context(torch, nbytes):
     return {"bytes_per_copy": 2 * n * 2, "ms": ms, "GB_s": 2 * n * 2 / (ms * 1e-3) / 1e9}
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.machine()
+
+
 def cpu_baseline(x, res, w, eps, budget_s):
     """The oracle (single-threaded scalar C) on whole prefill calls, repeated up to budget_s."""
     import oracle
@@ -232,7 +248,7 @@ def cpu_baseline(x, res, w, eps, budget_s):
         "sample": "whole W=%d H=%d T=%d call (all rows), %d repetitions, median %.1f ms, single thread"
                   % (W, H, T, len(times), med * 1e3),
         "ms_per_call": med * 1e3,
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_model(),
         "host_threads_available": os.cpu_count(),
     }
 

@@ -4,10 +4,10 @@
 // tutorial" (FlagTree PR #1122), section Summary and section Implementation 3:
 // reduced = sum of the W rank partials, residual_out = reduced + residual,
 // norm_out = RMSNorm(residual_out, weight, eps), on BF16 token rows.  Token rows
-// go to independent workgroups (section Implementation 2, "Row-parallel
-// execution"); the page says "approximately" one per row, which the split-H
-// variant (several workgroups per row, for few rows) and the sub-wave row groups
-// (several rows per wave, for small H) use.
+// go to independent workgroups (section Implementation 2, Row-parallel
+// execution).  The page's one-CTA-per-row mapping is only approximate there,
+// which leaves room for the split-H variant (several workgroups per row, for
+// few rows) and for sub-wave row groups (several rows per wave, for small H).
 //
 // Every variant performs the same IEEE operations per element:
 //   binary32 rank sum in rank order 0..W-1 starting from x_0, rounded once to BF16;
