@@ -92,6 +92,37 @@ class Pool:
         return out
 
 
+class ReduceCaller:
+    """Pre-marshalled arrms_reduce calls: W partials taken from the pool's partial and
+    residual tensors of consecutive slots, the output into a separate scratch area."""
+
+    def __init__(self, A, handle, pool, W, T, out_base, stream):
+        lib = A.load()
+        self.fn = lib.arrms_reduce
+        vp = ctypes.c_void_p
+        per_slot = pool.T // T
+        inputs_per_slot = pool.W + 1
+        self.args = []
+        te = pool.tensor_elems * 2
+        for j in range(per_slot):
+            for s in range(POOL_SLOTS):
+                parts = []
+                for r in range(W):
+                    slot = (s + r // inputs_per_slot) % POOL_SLOTS
+                    parts.append(pool.base + slot * (pool.W + 3) * te + (r % inputs_per_slot) * te + j * T * pool.H * 2)
+                out = out_base + s * te + j * T * pool.H * 2
+                self.args.append((vp(handle), (vp * W)(*parts), W, T, pool.H, vp(out)))
+        self.stream = vp(stream)
+        self.i = 0
+
+    def __call__(self):
+        a = self.args[self.i]
+        self.i = (self.i + 1) % len(self.args)
+        rc = self.fn(*a, self.stream)
+        if rc:
+            raise RuntimeError("arrms_reduce returned %d" % rc)
+
+
 class Caller:
     """Pre-marshalled ctypes arguments, so the host side of a call costs little."""
 
@@ -294,7 +325,7 @@ def main():
     x, res, w = synth.make_inputs(wl)
     pool = Pool(torch, x, res, w)
     log("pool: %d slots, %.2f GiB" % (POOL_SLOTS, pool.nbytes / 2 ** 30))
-    op = A.FusedReduceResidualRMSNorm(max_world=W, max_tokens=T, max_hidden=H, device=0)
+    op = A.FusedReduceResidualRMSNorm(max_world=8, max_tokens=T, max_hidden=H, device=0)
     stream = torch.cuda.current_stream().cuda_stream
 
     def caller(t):
@@ -365,6 +396,45 @@ def main():
                                    100 * row["frac_peak_back_to_back"], row["us_event_pair_p50"],
                                    row["us_isolated_p50"], row["us_graph_replay"]))
 
+    # ---- fusion: the page's two-stage form (rank sum kernel, then the epilogue as a
+    # one-rank fused call through a BF16 `reduced` tensor) against the fused call
+    fusion = None
+    reduce_sweep = []
+    if not args.no_sweep:
+        red_pool = torch.empty((POOL_SLOTS, T, H), dtype=torch.bfloat16, device="cuda")
+        rcall = ReduceCaller(A, op.handle, pool, W, T, red_pool.data_ptr(), stream)
+        epi_sets = [([red_pool.data_ptr() + (i % POOL_SLOTS) * T * H * 2], st[1], st[2], st[3])
+                    for i, st in enumerate(pool.sets(T))]
+        ecall = Caller(A, op.handle, epi_sets, 1, T, H, pool.weight.data_ptr(), eps, stream)
+
+        def two_stage():
+            rcall()
+            ecall()
+        for _ in range(50):
+            two_stage()
+        _, ts_ms = time_back_to_back(torch, two_stage, 1000)
+        _, red_ms = time_back_to_back(torch, rcall, 1000)
+        _, epi_ms = time_back_to_back(torch, ecall, 1000)
+        ts_bytes = nbytes + 2 * 2 * T * H  # plus writing and re-reading `reduced`
+        fusion = {"workload": "W=%d T=%d H=%d" % (W, T, H), "fused_us": gpu_ms * 1e3, "two_stage_us": ts_ms * 1e3,
+                  "reduce_kernel_us": red_ms * 1e3, "epilogue_kernel_us": epi_ms * 1e3,
+                  "two_stage_bytes": ts_bytes, "fused_bytes": nbytes,
+                  "fused_speedup": ts_ms / gpu_ms}
+        log("fusion: fused %.2f us vs two-stage %.2f us (reduce %.2f + epilogue %.2f): %.2fx" % (
+            gpu_ms * 1e3, ts_ms * 1e3, red_ms * 1e3, epi_ms * 1e3, ts_ms / gpu_ms))
+        # ---- the rank sum alone over sizes and W (reads W partials, writes reduced)
+        for w_ in (2, 4, 8):
+            for t in (16, 256, 4096):
+                c = ReduceCaller(A, op.handle, pool, w_, t, red_pool.data_ptr(), stream)
+                for _ in range(50):
+                    c()
+                _, ms = time_back_to_back(torch, c, 1000)
+                b = 2 * t * H * (w_ + 1)
+                reduce_sweep.append({"W": w_, "T": t, "H": H, "bytes": b, "us": ms * 1e3,
+                                     "GB_s": b / (ms * 1e-3) / 1e9})
+                log("reduce only W=%d T=%5d: %.2f us, %.0f GB/s" % (w_, t, ms * 1e3, b / (ms * 1e-3) / 1e9))
+        del red_pool
+
     copy = copy_context(torch, 512 * 2 ** 20)
     log("copy context: %.1f GB/s" % copy["GB_s"])
     tr = traffic_record()
@@ -400,6 +470,8 @@ def main():
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
         "sweep": sweep,
+        "fusion": fusion,
+        "reduce_only": reduce_sweep,
         "copy_context": copy,
         "device": {"name": props.name, "compute_units": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", None), "memory_GiB": props.total_memory / 2 ** 30},

@@ -56,6 +56,9 @@ extern "C" {
 #define ARRMS_VARIANT_ROW 1    /* one token row per workgroup (or per lane group) */
 #define ARRMS_VARIANT_SPLITH 2 /* each row split over several workgroups, two kernels */
 #define ARRMS_VARIANT_SCALAR 3 /* element-wise loads: any H, any 2-byte alignment */
+/* Plan kinds of arrms_reduce (the rank sum alone). */
+#define ARRMS_VARIANT_REDUCE 4        /* 16-byte vector loads, flat over T*H elements */
+#define ARRMS_VARIANT_REDUCE_SCALAR 5 /* element-wise, any 2-byte alignment */
 
 #define ARRMS_MAX_WORLD 16        /* largest W */
 #define ARRMS_MAX_HIDDEN 65536    /* largest H */
@@ -136,7 +139,9 @@ int arrms_destroy(arrms_handle_t h);
 /* Static text for a status code ("unknown status" for others). */
 const char* arrms_status_string(int status);
 
-/* hipError_t of the last failed HIP call on this handle (0 if none; -1 for a NULL handle). */
+/* hipError_t of the last failed HIP call on this handle (0 if none; -1 for a NULL handle).
+ * A HIP failure the library reports through its status is also cleared from HIP's
+ * per-thread last-error state, so it does not resurface in the caller's next check. */
 int arrms_last_hip_error(arrms_handle_t h);
 
 /* Force a variant (ARRMS_VARIANT_*) for later calls; AUTO restores per-shape choice.
@@ -165,6 +170,29 @@ int arrms_plan(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
 int arrms_query_plan(arrms_handle_t h, const void* const* partials, int world, int tokens,
                      int hidden, const void* residual, const void* weight, float eps,
                      const void* residual_out, const void* norm_out, arrms_plan_t* plan);
+
+/*
+ * The contract's first line on its own: reduced = BF16(sum over W partials),
+ * the rank sum of the page's collective stage (section Implementation 1) on
+ * this GPU's share, with the same arithmetic as arrms_fused (binary32 sum in
+ * rank order from partials[0], one rounding to BF16).  Together with
+ * arrms_fused(world = 1, partials = {reduced}) it forms the page's two-stage
+ * (collective, then epilogue) form of the operator, and gives the same bits as
+ * one arrms_fused call.
+ *   partials : HOST array of `world` device pointers, each BF16 [tokens][hidden]
+ *   reduced  : BF16 [tokens][hidden] output; may be exactly one of the partials,
+ *              may not otherwise overlap them
+ * Limits, 2-byte alignment, asynchrony and error behaviour as for arrms_fused;
+ * every pointer 16-byte aligned selects the vector kernel (any T*H), else the
+ * element-wise kernel.  Uses no workspace.
+ */
+int arrms_reduce(arrms_handle_t h, const void* const* partials, int world, int tokens, int hidden,
+                 void* reduced, hipStream_t stream);
+
+/* Host-only validation and planning of arrms_reduce (see arrms_plan). */
+int arrms_plan_reduce(int cu_count, const arrms_tuning_t* tuning, int max_world, int max_tokens,
+                      int max_hidden, const void* const* partials, int world, int tokens, int hidden,
+                      const void* reduced, arrms_plan_t* plan);
 
 #ifdef __cplusplus
 }

@@ -33,6 +33,8 @@ ARRMS_VARIANT_AUTO = 0
 ARRMS_VARIANT_ROW = 1
 ARRMS_VARIANT_SPLITH = 2
 ARRMS_VARIANT_SCALAR = 3
+ARRMS_VARIANT_REDUCE = 4
+ARRMS_VARIANT_REDUCE_SCALAR = 5
 
 ARRMS_MAX_WORLD = 16
 ARRMS_MAX_HIDDEN = 65536
@@ -40,7 +42,8 @@ ARRMS_ROW_MAX_HIDDEN = 16384
 
 # Every symbol include/arrms.h declares.
 EXPORTS = ("arrms_create", "arrms_fused", "arrms_destroy", "arrms_status_string", "arrms_last_hip_error",
-           "arrms_set_variant", "arrms_set_tuning", "arrms_plan", "arrms_query_plan")
+           "arrms_set_variant", "arrms_set_tuning", "arrms_plan", "arrms_query_plan", "arrms_reduce",
+           "arrms_plan_reduce")
 
 
 class arrms_plan_t(ctypes.Structure):
@@ -92,6 +95,9 @@ def load() -> ctypes.CDLL:
                                        ci, ci, vp, vp, cf, vp, vp, ctypes.POINTER(arrms_plan_t)]
             lib.arrms_query_plan.argtypes = [vp, ctypes.POINTER(vp), ci, ci, ci, vp, vp, cf, vp, vp,
                                              ctypes.POINTER(arrms_plan_t)]
+            lib.arrms_reduce.argtypes = [vp, ctypes.POINTER(vp), ci, ci, ci, vp, vp]
+            lib.arrms_plan_reduce.argtypes = [ci, ctypes.POINTER(arrms_tuning_t), ci, ci, ci, ctypes.POINTER(vp), ci,
+                                              ci, ci, vp, ctypes.POINTER(arrms_plan_t)]
             _lib = lib
     return _lib
 
@@ -153,6 +159,22 @@ def arrms_query_plan(h, partials: Optional[Sequence[int]], world: int, tokens: i
     p = arrms_plan_t()
     rc = load().arrms_query_plan(h, _ptrs(partials), world, tokens, hidden, residual, weight, eps, residual_out,
                                  norm_out, ctypes.byref(p))
+    return rc, p.as_dict()
+
+
+def arrms_reduce(h, partials: Optional[Sequence[int]], world: int, tokens: int, hidden: int, reduced: int,
+                 stream: int = 0) -> int:
+    return load().arrms_reduce(h, _ptrs(partials), world, tokens, hidden, reduced, stream)
+
+
+def arrms_plan_reduce(cu_count: int, tuning: Optional[arrms_tuning_t], max_world: int, max_tokens: int,
+                      max_hidden: int, partials: Optional[Sequence[int]], world: int, tokens: int, hidden: int,
+                      reduced: int):
+    """Host-only validation and planning of arrms_reduce. Returns (status, plan dict)."""
+    p = arrms_plan_t()
+    rc = load().arrms_plan_reduce(cu_count, ctypes.byref(tuning) if tuning is not None else None, max_world,
+                                  max_tokens, max_hidden, _ptrs(partials), world, tokens, hidden, reduced,
+                                  ctypes.byref(p))
     return rc, p.as_dict()
 
 
@@ -229,6 +251,22 @@ class FusedReduceResidualRMSNorm:
         if rc != ARRMS_OK:
             raise ArrmsError(rc, "arrms_fused")
         return residual_out, norm_out
+
+    def reduce(self, partials, reduced=None, stream=None):
+        """reduced = BF16 rank sum of the partials ([W, T, H] or W x [T, H]); returns reduced."""
+        import torch
+        parts = list(partials.unbind(0)) if isinstance(partials, torch.Tensor) and partials.dim() == 3 else list(partials)
+        T, H = parts[0].shape
+        for i, p in enumerate(parts):
+            self._check(p, "partials[%d]" % i, (T, H))
+        if reduced is None:
+            reduced = torch.empty_like(parts[0])
+        self._check(reduced, "reduced", (T, H))
+        s = (stream if stream is not None else torch.cuda.current_stream(self.device)).cuda_stream
+        rc = arrms_reduce(self.handle, [q.data_ptr() for q in parts], len(parts), T, H, reduced.data_ptr(), s)
+        if rc != ARRMS_OK:
+            raise ArrmsError(rc, "arrms_reduce")
+        return reduced
 
     def close(self) -> None:
         """Destroy the handle (synchronise the stream of the last call first)."""

@@ -303,6 +303,97 @@ int arrms_plan(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
     return ARRMS_OK;
 }
 
+int arrms_plan_reduce(int cu_count, const arrms_tuning_t* tuning, int max_world, int max_tokens, int max_hidden,
+                      const void* const* partials, int world, int tokens, int hidden, const void* reduced,
+                      arrms_plan_t* plan) {
+    if (!plan) return ARRMS_ERR_INVALID_ARG;
+    memset(plan, 0, sizeof *plan);
+    if (cu_count < 1 || max_world < 1 || max_world > ARRMS_MAX_WORLD || max_tokens < 0 || max_hidden < 1 ||
+        max_hidden > ARRMS_MAX_HIDDEN)
+        return ARRMS_ERR_INVALID_ARG;
+    if (!valid_tuning(tuning)) return ARRMS_ERR_INVALID_ARG;
+    if (world < 1 || world > max_world) return ARRMS_ERR_INVALID_ARG;
+    if (tokens < 0 || tokens > max_tokens) return ARRMS_ERR_INVALID_ARG;
+    if (hidden < 1 || hidden > max_hidden) return ARRMS_ERR_INVALID_ARG;
+    if (tokens == 0) return ARRMS_OK;
+    if (!partials || !reduced) return ARRMS_ERR_INVALID_ARG;
+    uintptr_t any = reinterpret_cast<uintptr_t>(reduced);
+    for (int r = 0; r < world; ++r) {
+        if (!partials[r]) return ARRMS_ERR_INVALID_ARG;
+        any |= reinterpret_cast<uintptr_t>(partials[r]);
+    }
+    if (any & 1u) return ARRMS_ERR_INVALID_ARG;
+    const long long count = static_cast<long long>(tokens) * hidden;
+    const size_t n = static_cast<size_t>(count) * 2;
+    // The output may be exactly one of the partials (each element is read before it is written).
+    for (int r = 0; r < world; ++r)
+        if (reduced != partials[r] && overlap(reduced, n, partials[r], n)) return ARRMS_ERR_INVALID_ARG;
+    plan->kernels = 1;
+    plan->rows_per_block = 1;
+    plan->chunks_per_row = 1;
+    plan->block = 256;
+    plan->threads_per_row = 256;
+    if (any & 15u) {
+        const long long want = (count + 255) / 256;
+        const long long cap = 8LL * cu_count;
+        plan->variant = ARRMS_VARIANT_REDUCE_SCALAR;
+        plan->blocks = static_cast<int>(want < cap ? want : cap);
+        plan->grid = plan->blocks;
+        return ARRMS_OK;
+    }
+    const int vpt = arrms::reduce_vpt(world);
+    const long long nvec = count / 8;
+    const long long per_block = 256LL * vpt;
+    long long blocks = (nvec + per_block - 1) / per_block;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 0x7ffffff0LL) return ARRMS_ERR_UNSUPPORTED;
+    plan->variant = ARRMS_VARIANT_REDUCE;
+    plan->vec_per_thread = vpt;
+    plan->blocks = static_cast<int>(blocks);
+    int k = 0;
+    if (plan->blocks >= 64) {
+        const long block_bytes = 16L * per_block * (world + 1);
+        k = 1;
+        while (2L * k * block_bytes <= kXcdRunBytes) k *= 2;
+    }
+    finish_vector_plan(tuning, plan, k);
+    return ARRMS_OK;
+}
+
+int arrms_reduce(arrms_handle_t h, const void* const* partials, int world, int tokens, int hidden, void* reduced,
+                 hipStream_t stream) {
+    if (!h) return ARRMS_ERR_INVALID_ARG;
+    arrms_plan_t p;
+    const int rc = arrms_plan_reduce(h->cu_count, h->has_tuning ? &h->tuning : nullptr, h->max_world, h->max_tokens,
+                                     h->max_hidden, partials, world, tokens, hidden, reduced, &p);
+    if (rc != ARRMS_OK || p.grid == 0) return rc;
+    arrms::Args a;
+    memset(&a, 0, sizeof a);
+    for (int r = 0; r < world; ++r) a.x.p[r] = partials[r];
+    a.reduced = reduced;
+    a.world = world;
+    a.tokens = tokens;
+    a.hidden = hidden;
+    a.count = static_cast<long long>(tokens) * hidden;
+    a.blocks = p.blocks;
+    a.xcd_chunk = p.xcd_chunk;
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != h->device && hipSetDevice(h->device) != hipSuccess) {
+        h->last_hip_error = static_cast<int>(hipErrorInvalidDevice);
+        return ARRMS_ERR_HIP;
+    }
+    const hipError_t e = p.variant == ARRMS_VARIANT_REDUCE ? arrms::launch_reduce(a, p.grid, p.block, stream)
+                                                           : arrms::launch_reduce_scalar(a, p.grid, p.block, stream);
+    if (prev >= 0 && prev != h->device) (void)hipSetDevice(prev);
+    if (e != hipSuccess) {
+        h->last_hip_error = static_cast<int>(e);
+        (void)hipGetLastError();  // reported through the status and arrms_last_hip_error
+        return ARRMS_ERR_HIP;
+    }
+    return ARRMS_OK;
+}
+
 int arrms_create(arrms_handle_t* out, int device, int max_world, int max_tokens, int max_hidden) {
     if (!out) return ARRMS_ERR_INVALID_ARG;
     *out = nullptr;
@@ -341,7 +432,10 @@ int arrms_create(arrms_handle_t* out, int device, int max_world, int max_tokens,
     int rc = ARRMS_OK;
     const size_t rows = max_tokens > 0 ? static_cast<size_t>(max_tokens) : 1;
     const hipError_t e = hipMalloc(reinterpret_cast<void**>(&h->ws), rows * h->ws_chunks * sizeof(double));
-    if (e != hipSuccess) rc = (e == hipErrorOutOfMemory) ? ARRMS_ERR_OOM : ARRMS_ERR_HIP;
+    if (e != hipSuccess) {
+        rc = (e == hipErrorOutOfMemory) ? ARRMS_ERR_OOM : ARRMS_ERR_HIP;
+        (void)hipGetLastError();  // reported here; leave no stale error for the caller's next launch check
+    }
     if (rc != ARRMS_OK) {
         if (h->ws) (void)hipFree(h->ws);
         delete h;
@@ -435,6 +529,7 @@ int arrms_fused(arrms_handle_t h, const void* const* partials, int world, int to
     if (prev >= 0 && prev != h->device) (void)hipSetDevice(prev);
     if (e != hipSuccess) {
         h->last_hip_error = static_cast<int>(e);
+        (void)hipGetLastError();  // reported through the status and arrms_last_hip_error
         return ARRMS_ERR_HIP;
     }
     return ARRMS_OK;

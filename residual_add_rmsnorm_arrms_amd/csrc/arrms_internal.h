@@ -23,6 +23,7 @@ struct Args {
     const void* weight;     // BF16 [hidden]
     void* residual_out;     // BF16 [tokens][hidden]; may equal residual
     void* norm_out;         // BF16 [tokens][hidden]
+    void* reduced;          // rank sum only: BF16 [tokens][hidden] output
     double* ws;             // split-H: [tokens][chunks] binary64 partial sums of squares
     double hidden_d;        // H as binary64 (the divisor of the mean of squares)
     float eps;
@@ -36,6 +37,7 @@ struct Args {
     int chunk_vec;          // split-H: vectors per chunk
     int blocks;             // logical workgroups (the launched grid may add XCD padding)
     int xcd_chunk;          // K > 0: runs of K consecutive blocks per XCD (grid a multiple of 8K)
+    long long count;        // rank sum only: elements (tokens * hidden)
 };
 
 // Each launcher returns the hipError_t of the launch itself.
@@ -43,5 +45,11 @@ hipError_t launch_row(const Args& a, int vec_per_thread, int grid, int block, hi
 // Split-H launches two kernels on `s`: the partial pass, then the norm pass.
 hipError_t launch_splith(const Args& a, int vec_per_thread, int grid, int block, hipStream_t s);
 hipError_t launch_scalar(const Args& a, int grid, int block, hipStream_t s);
+// Rank sum only (reduced = BF16 sum of the partials), flat over a.count elements.
+// 16-byte vectors per lane per partial in reduce_kernel (fewer for the 16-wide
+// rank arrays of W > 8, to stay within the register budget).
+constexpr int reduce_vpt(int world) { return (world >= 1 && world <= 8) ? 4 : 1; }
+hipError_t launch_reduce(const Args& a, int grid, int block, hipStream_t s);
+hipError_t launch_reduce_scalar(const Args& a, int grid, int block, hipStream_t s);
 
 }  // namespace arrms

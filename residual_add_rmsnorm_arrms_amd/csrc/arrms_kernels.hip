@@ -143,22 +143,43 @@ __device__ __forceinline__ float inv_rms(double sum_sq, double hidden, float eps
 // ------------------------------------------------------- per-vector arithmetic
 // Rank sum, reduced rounding and residual add for one 16-byte vector (8
 // elements) of a row; accumulates the squares into ss and returns residual_out.
+// binary32 rank sum, in rank order from x_0, of the two elements in dword j.
+template <int W>
+__device__ __forceinline__ void rank_sum(const u32x4 (&xv)[W > 0 ? W : kMaxWorld], int world, int j, float& a_lo,
+                                         float& a_hi) {
+    constexpr int WA = W > 0 ? W : kMaxWorld;
+    a_lo = lo_f32(xv[0][j]);
+    a_hi = hi_f32(xv[0][j]);
+#pragma unroll
+    for (int r = 1; r < WA; ++r) {
+        if (W > 0 || r < world) {
+            a_lo = a_lo + lo_f32(xv[r][j]);
+            a_hi = a_hi + hi_f32(xv[r][j]);
+        }
+    }
+}
+
+// `reduced` for one vector: the rank sum rounded to BF16.
+template <int W>
+__device__ __forceinline__ u32x4 reduced_vec(const u32x4 (&xv)[W > 0 ? W : kMaxWorld], int world) {
+    u32x4 out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float a_lo, a_hi;
+        rank_sum<W>(xv, world, j, a_lo, a_hi);
+        out[j] = pack2(round_bf16(a_lo), round_bf16(a_hi));
+    }
+    return out;
+}
+
 template <int W>
 __device__ __forceinline__ u32x4 residual_vec(const u32x4 (&xv)[W > 0 ? W : kMaxWorld], int world,
                                               u32x4 rv, double& ss) {
-    constexpr int WA = W > 0 ? W : kMaxWorld;
     u32x4 ro;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        float a_lo = lo_f32(xv[0][j]);
-        float a_hi = hi_f32(xv[0][j]);
-#pragma unroll
-        for (int r = 1; r < WA; ++r) {
-            if (W > 0 || r < world) {
-                a_lo = a_lo + lo_f32(xv[r][j]);
-                a_hi = a_hi + hi_f32(xv[r][j]);
-            }
-        }
+        float a_lo, a_hi;
+        rank_sum<W>(xv, world, j, a_lo, a_hi);
         const uint32_t o_lo = round_bf16(__uint_as_float(round_bf16(a_lo)) + lo_f32(rv[j]));
         const uint32_t o_hi = round_bf16(__uint_as_float(round_bf16(a_hi)) + hi_f32(rv[j]));
         const double d_lo = static_cast<double>(__uint_as_float(o_lo));
@@ -372,6 +393,55 @@ __global__ void __launch_bounds__(256) scalar_kernel(const Args a) {
     }
 }
 
+// ------------------------------------------------------------ rank sum only
+// The contract's first line on its own (the page's collective stage, locally):
+// reduced = BF16(sum of the W partials), flat over a.count = T*H elements.
+// Each lane sums VPT 16-byte vectors (at stride blockDim) of every partial;
+// the last count % 8 elements go element-wise in the last block.
+template <int W>
+__global__ void __launch_bounds__(256) reduce_kernel(const Args a) {
+    constexpr int WA = W > 0 ? W : kMaxWorld;
+    constexpr int kReduceVpt = reduce_vpt(W > 0 ? W : kMaxWorld);
+    const int world = W > 0 ? W : a.world;
+    const int block = logical_block(a);
+    if (block < 0) return;
+    const size_t nvec = static_cast<size_t>(a.count) / 8;
+    const size_t first = static_cast<size_t>(block) * blockDim.x * kReduceVpt + threadIdx.x;
+    bool ok[kReduceVpt];
+    u32x4 xv[kReduceVpt][WA];
+#pragma unroll
+    for (int k = 0; k < kReduceVpt; ++k) {
+        const size_t v = first + static_cast<size_t>(k) * blockDim.x;
+        ok[k] = v < nvec;
+        if (ok[k]) {
+#pragma unroll
+            for (int r = 0; r < WA; ++r)
+                if (W > 0 || r < world) xv[k][r] = ld4_stream(a.x.p[r], v);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kReduceVpt; ++k)
+        if (ok[k]) st4_stream(a.reduced, first + static_cast<size_t>(k) * blockDim.x, reduced_vec<W>(xv[k], world));
+    if (block == a.blocks - 1) {  // the count % 8 elements past the last whole vector
+        for (size_t e = nvec * 8 + threadIdx.x; e < static_cast<size_t>(a.count); e += blockDim.x) {
+            float acc = lo_f32(static_cast<const uint16_t*>(a.x.p[0])[e]);
+            for (int r = 1; r < world; ++r) acc = acc + lo_f32(static_cast<const uint16_t*>(a.x.p[r])[e]);
+            static_cast<uint16_t*>(a.reduced)[e] = static_cast<uint16_t>(round_bf16(acc) >> 16);
+        }
+    }
+}
+
+// Rank sum only, element-wise, for pointers that are not 16-byte aligned.
+__global__ void __launch_bounds__(256) reduce_scalar_kernel(const Args a) {
+    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+    for (size_t e = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < static_cast<size_t>(a.count);
+         e += stride) {
+        float acc = lo_f32(static_cast<const uint16_t*>(a.x.p[0])[e]);
+        for (int r = 1; r < a.world; ++r) acc = acc + lo_f32(static_cast<const uint16_t*>(a.x.p[r])[e]);
+        static_cast<uint16_t*>(a.reduced)[e] = static_cast<uint16_t>(round_bf16(acc) >> 16);
+    }
+}
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch(const void* fn, const Args& a, int grid, int block, hipStream_t s) {
     void* args[] = {const_cast<Args*>(&a)};
@@ -426,7 +496,29 @@ const void* splith_fn(int world) {
     return nullptr;
 }
 
+const void* reduce_fn(int world) {
+    switch (world) {
+        case 1: return reinterpret_cast<const void*>(&reduce_kernel<1>);
+        case 2: return reinterpret_cast<const void*>(&reduce_kernel<2>);
+        case 3: return reinterpret_cast<const void*>(&reduce_kernel<3>);
+        case 4: return reinterpret_cast<const void*>(&reduce_kernel<4>);
+        case 5: return reinterpret_cast<const void*>(&reduce_kernel<5>);
+        case 6: return reinterpret_cast<const void*>(&reduce_kernel<6>);
+        case 7: return reinterpret_cast<const void*>(&reduce_kernel<7>);
+        case 8: return reinterpret_cast<const void*>(&reduce_kernel<8>);
+        default: return reinterpret_cast<const void*>(&reduce_kernel<0>);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_reduce(const Args& a, int grid, int block, hipStream_t s) {
+    return launch(reduce_fn(a.world), a, grid, block, s);
+}
+
+hipError_t launch_reduce_scalar(const Args& a, int grid, int block, hipStream_t s) {
+    return launch(reinterpret_cast<const void*>(&reduce_scalar_kernel), a, grid, block, s);
+}
 
 hipError_t launch_row(const Args& a, int vpt, int grid, int block, hipStream_t s) {
     const void* fn = nullptr;

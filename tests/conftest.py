@@ -26,3 +26,15 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    import sys
+    mod = sys.modules.get("tests.gpu_util")
+    stats = getattr(mod, "STATS", None) if mod else None
+    if stats:
+        cases = len(stats)
+        diff = sum(n for _, n, _ in stats)
+        total = sum(t for _, _, t in stats)
+        terminalreporter.write_line("GPU parity: %d checks, norm_out not bit-identical to the oracle in %d of %d "
+                                    "elements; residual_out bit-identical in all" % (cases, diff, total))

@@ -25,6 +25,8 @@ NORM_MAX_ULP = 2
 NORM_MAX_ABS = 0.03125
 
 _op = None
+# (case, norm_out elements not bit-identical, elements) of every parity check, for the summary
+STATS = []
 
 
 def op() -> A.FusedReduceResidualRMSNorm:
@@ -78,7 +80,9 @@ def assert_parity(got_ro, got_no, ref, where="") -> int:
         e = np.abs(gv[fin] - wv[fin])
         assert d.max() <= NORM_MAX_ULP and e.max() <= NORM_MAX_ABS, (
             "%s: norm_out off by up to %d BF16 steps / %g" % (where, int(d.max()), float(e.max())))
-    return int((got_no[fin] != want_no[fin]).sum())
+    n = int((got_no[fin] != want_no[fin]).sum())
+    STATS.append((where, n, int(got_no.size)))
+    return n
 
 
 def inputs(W, T, H, seed=0, sigma=1.0, eps=1e-6, outlier_p=0.0):

@@ -249,3 +249,34 @@ def test_measured_automatic_choices(W, T, H, variant, vpt, tpr, k):
     rc, p = plan(W, T, H)
     assert rc == A.ARRMS_OK
     assert (p["variant"], p["vec_per_thread"], p["threads_per_row"], p["xcd_chunk"]) == (variant, vpt, tpr, k)
+
+
+def rplan(W, T, H, lim=LIM, **over):
+    b = bufs(W, T, H)
+    b.update(over)
+    return A.arrms_plan_reduce(CU, None, lim["max_world"], lim["max_tokens"], lim["max_hidden"], b["partials"], W, T,
+                               H, b.get("reduced", b["residual_out"]))
+
+
+@pytest.mark.parametrize("W,T,H", [(4, 4096, 2048), (8, 16383, 5120), (2, 1, 8), (3, 7, 3), (16, 5, 1000), (11, 3, 2048)])
+def test_reduce_plans_cover_every_element(W, T, H):
+    rc, p = rplan(W, T, H)
+    assert rc == A.ARRMS_OK and p["variant"] == A.ARRMS_VARIANT_REDUCE
+    nvec = T * H // 8
+    per_block = p["block"] * p["vec_per_thread"]
+    assert p["blocks"] == max(1, -(-nvec // per_block)) and p["grid"] == grid_of(p)
+    assert p["vec_per_thread"] == (4 if W <= 8 else 1)
+
+
+def test_reduce_plan_validation():
+    b = bufs(4, 16, 2048)
+    assert rplan(4, 16, 2048, reduced=b["residual"] + 2)[1]["variant"] == A.ARRMS_VARIANT_REDUCE_SCALAR
+    assert rplan(4, 16, 2048, reduced=b["partials"][1])[0] == A.ARRMS_OK              # in place into one partial
+    assert rplan(4, 16, 2048, reduced=b["partials"][1] + 64)[0] == A.ARRMS_ERR_INVALID_ARG
+    assert rplan(4, 16, 2048, reduced=0)[0] == A.ARRMS_ERR_INVALID_ARG
+    assert rplan(4, 16, 2048, reduced=b["residual"] + 1)[0] == A.ARRMS_ERR_INVALID_ARG
+    assert rplan(17, 16, 2048)[0] == A.ARRMS_ERR_INVALID_ARG
+    assert rplan(4, 20001, 2048)[0] == A.ARRMS_ERR_INVALID_ARG
+    rc, p = A.arrms_plan_reduce(CU, None, 4, 10, 2048, None, 4, 0, 2048, 0)
+    assert rc == A.ARRMS_OK and p["grid"] == 0
+    assert A.arrms_reduce(None, b["partials"], 4, 16, 2048, b["residual_out"], 0) == A.ARRMS_ERR_INVALID_ARG

@@ -308,3 +308,6 @@ def test_create_destroy_cycles():
         assert A.arrms_destroy(h) == A.ARRMS_OK
     rc, h = A.arrms_create(0, 4, 2 ** 31 - 1, 65536)  # workspace far beyond device memory
     assert rc == A.ARRMS_ERR_OOM and h is None
+    # the failed allocation leaves no stale error behind for the next launch check
+    torch.zeros(1000, device="cuda").add_(1)
+    torch.cuda.synchronize()

@@ -1,0 +1,85 @@
+"""GPU parity of the rank sum alone (arrms_reduce) and of the page's two-stage form
+(rank sum, then the residual + RMSNorm epilogue as arrms_fused with W=1) against the
+CPU oracle's `reduced`, `residual_out` and `norm_out`."""
+import numpy as np
+import pytest
+import torch
+
+import residual_add_rmsnorm_arrms_amd as A
+import synth
+from tests.gpu_util import assert_parity, inputs, op, reference, run, say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0)
+
+
+def reduce_gpu(x, reduced=None):
+    o = op()
+    xd = x.to(DEV)
+    out = o.reduce(xd, reduced)
+    torch.cuda.synchronize()
+    return synth.bits(out.cpu())
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8, 9, 16])
+@pytest.mark.parametrize("T,H", [(1, 8), (3, 3), (5, 1001), (37, 2048), (4096, 2048), (7, 5120)])
+def test_reduce_matches_oracle(W, T, H):
+    say("case reduce W=%d T=%d H=%d" % (W, T, H))
+    x, res, w = inputs(W, T, H, seed=300 + W + T, outlier_p=0.01)
+    got = reduce_gpu(x)
+    want = reference(x, res, w, 1e-6)["reduced"]
+    bad = np.flatnonzero(got.ravel() != want.ravel())
+    assert bad.size == 0, "%d reduced elements differ" % bad.size
+
+
+def test_reduce_full_size_ragged_outliers():
+    wl = synth.WORKLOADS["ragged_outliers"]
+    say("case reduce full size %s" % wl.name)
+    x, res, w = synth.make_inputs(wl)
+    got = reduce_gpu(x)
+    want = reference(x, res, w, wl.eps)["reduced"]
+    assert np.array_equal(got, want)
+
+
+def test_reduce_in_place_into_a_partial():
+    say("case reduce in place")
+    x, res, w = inputs(4, 33, 2048, seed=301)
+    xd = x.to(DEV)
+    out = op().reduce(xd, reduced=xd[2])
+    torch.cuda.synchronize()
+    assert np.array_equal(synth.bits(out.cpu()), reference(x, res, w, 1e-6)["reduced"])
+
+
+def test_reduce_misaligned_uses_element_path():
+    say("case reduce misaligned")
+    W, T, H = 3, 11, 2048
+    x, res, w = inputs(W, T, H, seed=302)
+    n = T * H
+    parts = []
+    for r in range(W):
+        buf = torch.zeros(n + 8, dtype=torch.bfloat16, device=DEV)
+        v = buf[1:1 + n].view(T, H)
+        v.copy_(x[r].to(DEV))
+        parts.append(v)
+    out = torch.zeros(n + 8, dtype=torch.bfloat16, device=DEV)[1:1 + n].view(T, H)
+    rc, plan = A.arrms_plan_reduce(256, None, 16, 20000, 65536, [p.data_ptr() for p in parts], W, T, H, out.data_ptr())
+    assert rc == A.ARRMS_OK and plan["variant"] == A.ARRMS_VARIANT_REDUCE_SCALAR
+    op().reduce(parts, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(synth.bits(out.cpu()), reference(x, res, w, 1e-6)["reduced"])
+
+
+@pytest.mark.parametrize("W,T,H", [(4, 4096, 2048), (8, 129, 5120), (2, 4, 128)])
+def test_two_stage_form_equals_fused(W, T, H):
+    """Rank sum, then the epilogue as a one-rank fused call: the same bits as one fused call."""
+    say("case two-stage W=%d T=%d H=%d" % (W, T, H))
+    x, res, w = inputs(W, T, H, seed=303 + T)
+    o = op()
+    xd, rd, wd = x.to(DEV), res.to(DEV), w.to(DEV)
+    red = o.reduce(xd)
+    ro2, no2 = o([red], rd, wd, 1e-6)
+    ro1, no1 = o(xd, rd, wd, 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(ro1.view(torch.int16), ro2.view(torch.int16))
+    assert torch.equal(no1.view(torch.int16), no2.view(torch.int16))
+    assert_parity(synth.bits(ro2.cpu()), synth.bits(no2.cpu()), reference(x, res, w, 1e-6), "two-stage")
