@@ -40,6 +40,10 @@ constexpr int kMinChunkVec = 64;
 constexpr int kMaxLiveVectors = 40;
 // Traffic of one automatic XCD run of the row variant.
 constexpr long kXcdRunBytes = 3L << 20;
+// Vectors per lane of the rank-sum-only kernel (measured on MI355X at W=2/4/8,
+// T=4096, H=2048: one vector per lane with ~3 MiB XCD runs is fastest, e.g.
+// 5.6 TB/s at W=4 against 5.1 TB/s with four vectors per lane).
+constexpr int kReduceAutoVpt = 1;
 // Rows with less traffic than this never use split-H automatically.
 constexpr long kSplitMinRowBytes = 96L << 10;
 
@@ -341,7 +345,13 @@ int arrms_plan_reduce(int cu_count, const arrms_tuning_t* tuning, int max_world,
         plan->grid = plan->blocks;
         return ARRMS_OK;
     }
-    const int vpt = arrms::reduce_vpt(world);
+    int vpt = kReduceAutoVpt;
+    if (tuning && tuning->vec_per_thread) vpt = tuning->vec_per_thread;
+    if (world > 8) {
+        if (tuning && tuning->vec_per_thread > 1) return ARRMS_ERR_UNSUPPORTED;
+        vpt = 1;
+    }
+    if (vpt > 4) return ARRMS_ERR_UNSUPPORTED;
     const long long nvec = count / 8;
     const long long per_block = 256LL * vpt;
     long long blocks = (nvec + per_block - 1) / per_block;
@@ -383,7 +393,7 @@ int arrms_reduce(arrms_handle_t h, const void* const* partials, int world, int t
         h->last_hip_error = static_cast<int>(hipErrorInvalidDevice);
         return ARRMS_ERR_HIP;
     }
-    const hipError_t e = p.variant == ARRMS_VARIANT_REDUCE ? arrms::launch_reduce(a, p.grid, p.block, stream)
+    const hipError_t e = p.variant == ARRMS_VARIANT_REDUCE ? arrms::launch_reduce(a, p.vec_per_thread, p.grid, p.block, stream)
                                                            : arrms::launch_reduce_scalar(a, p.grid, p.block, stream);
     if (prev >= 0 && prev != h->device) (void)hipSetDevice(prev);
     if (e != hipSuccess) {

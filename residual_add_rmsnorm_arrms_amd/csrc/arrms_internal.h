@@ -46,10 +46,9 @@ hipError_t launch_row(const Args& a, int vec_per_thread, int grid, int block, hi
 hipError_t launch_splith(const Args& a, int vec_per_thread, int grid, int block, hipStream_t s);
 hipError_t launch_scalar(const Args& a, int grid, int block, hipStream_t s);
 // Rank sum only (reduced = BF16 sum of the partials), flat over a.count elements.
-// 16-byte vectors per lane per partial in reduce_kernel (fewer for the 16-wide
-// rank arrays of W > 8, to stay within the register budget).
-constexpr int reduce_vpt(int world) { return (world >= 1 && world <= 8) ? 4 : 1; }
-hipError_t launch_reduce(const Args& a, int grid, int block, hipStream_t s);
+// reduce_kernel instances: 16-byte vectors per lane per partial of 1, 2 or 4
+// for W <= 8, only 1 for the 16-wide rank arrays of larger W (register budget).
+hipError_t launch_reduce(const Args& a, int vec_per_thread, int grid, int block, hipStream_t s);
 hipError_t launch_reduce_scalar(const Args& a, int grid, int block, hipStream_t s);
 
 }  // namespace arrms

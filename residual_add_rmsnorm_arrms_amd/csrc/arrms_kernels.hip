@@ -398,10 +398,9 @@ __global__ void __launch_bounds__(256) scalar_kernel(const Args a) {
 // reduced = BF16(sum of the W partials), flat over a.count = T*H elements.
 // Each lane sums VPT 16-byte vectors (at stride blockDim) of every partial;
 // the last count % 8 elements go element-wise in the last block.
-template <int W>
+template <int W, int kReduceVpt>
 __global__ void __launch_bounds__(256) reduce_kernel(const Args a) {
     constexpr int WA = W > 0 ? W : kMaxWorld;
-    constexpr int kReduceVpt = reduce_vpt(W > 0 ? W : kMaxWorld);
     const int world = W > 0 ? W : a.world;
     const int block = logical_block(a);
     if (block < 0) return;
@@ -496,24 +495,35 @@ const void* splith_fn(int world) {
     return nullptr;
 }
 
+template <int VPT>
 const void* reduce_fn(int world) {
     switch (world) {
-        case 1: return reinterpret_cast<const void*>(&reduce_kernel<1>);
-        case 2: return reinterpret_cast<const void*>(&reduce_kernel<2>);
-        case 3: return reinterpret_cast<const void*>(&reduce_kernel<3>);
-        case 4: return reinterpret_cast<const void*>(&reduce_kernel<4>);
-        case 5: return reinterpret_cast<const void*>(&reduce_kernel<5>);
-        case 6: return reinterpret_cast<const void*>(&reduce_kernel<6>);
-        case 7: return reinterpret_cast<const void*>(&reduce_kernel<7>);
-        case 8: return reinterpret_cast<const void*>(&reduce_kernel<8>);
-        default: return reinterpret_cast<const void*>(&reduce_kernel<0>);
+        case 1: return reinterpret_cast<const void*>(&reduce_kernel<1, VPT>);
+        case 2: return reinterpret_cast<const void*>(&reduce_kernel<2, VPT>);
+        case 3: return reinterpret_cast<const void*>(&reduce_kernel<3, VPT>);
+        case 4: return reinterpret_cast<const void*>(&reduce_kernel<4, VPT>);
+        case 5: return reinterpret_cast<const void*>(&reduce_kernel<5, VPT>);
+        case 6: return reinterpret_cast<const void*>(&reduce_kernel<6, VPT>);
+        case 7: return reinterpret_cast<const void*>(&reduce_kernel<7, VPT>);
+        case 8: return reinterpret_cast<const void*>(&reduce_kernel<8, VPT>);
+        default: break;
     }
+    if constexpr (VPT == 1) return reinterpret_cast<const void*>(&reduce_kernel<0, 1>);
+    return nullptr;
 }
 
 }  // namespace
 
-hipError_t launch_reduce(const Args& a, int grid, int block, hipStream_t s) {
-    return launch(reduce_fn(a.world), a, grid, block, s);
+hipError_t launch_reduce(const Args& a, int vpt, int grid, int block, hipStream_t s) {
+    const void* fn = nullptr;
+    switch (vpt) {
+        case 1: fn = reduce_fn<1>(a.world); break;
+        case 2: fn = reduce_fn<2>(a.world); break;
+        case 4: fn = reduce_fn<4>(a.world); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (!fn) return hipErrorInvalidValue;
+    return launch(fn, a, grid, block, s);
 }
 
 hipError_t launch_reduce_scalar(const Args& a, int grid, int block, hipStream_t s) {

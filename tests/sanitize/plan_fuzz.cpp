@@ -1,0 +1,93 @@
+// Host-only fuzz of the library's argument validation and launch planning
+// (arrms_plan, arrms_plan_reduce), built with g++ under AddressSanitizer and
+// UndefinedBehaviorSanitizer.  The kernel launchers are replaced by stubs: the
+// planner never launches.  Pointers are fake integers; they are compared, never
+// dereferenced.  Exit status 0 and no sanitizer report = pass.
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "arrms.h"
+#include "arrms_internal.h"
+
+namespace arrms {
+hipError_t launch_row(const Args&, int, int, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_splith(const Args&, int, int, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_scalar(const Args&, int, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_reduce(const Args&, int, int, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_reduce_scalar(const Args&, int, int, hipStream_t) { return hipErrorInvalidValue; }
+}  // namespace arrms
+
+static uint64_t state = 0x243F6A8885A308D3ull;
+static uint64_t next() {  // SplitMix64
+    uint64_t z = (state += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+static int pick(const int* v, int n) { return v[next() % n]; }
+
+static int fail(const char* what, int i) {
+    fprintf(stderr, "check failed: %s (iteration %d)\n", what, i);
+    return 1;
+}
+
+int main(int argc, char** argv) {
+    const int iters = argc > 1 ? atoi(argv[1]) : 200000;
+    const int worlds[] = {-1, 0, 1, 2, 3, 4, 5, 8, 9, 12, 16, 17};
+    const int tokens[] = {-5, 0, 1, 2, 3, 16, 17, 64, 255, 256, 1000, 4096, 16383, 100000};
+    const int hiddens[] = {-1, 0, 1, 3, 8, 64, 128, 1000, 1001, 2048, 5120, 8192, 16384, 16392, 24576, 65536, 65537};
+    const int tvpt[] = {0, 0, 0, 1, 2, 3, 4, 8};
+    const int ttpr[] = {0, 0, 0, 16, 32, 48, 64, 128, 256, 320, 512, 1024, 2048};
+    const int tblk[] = {0, 0, 64, 100, 256, 1024, 2048};
+    const int tspl[] = {-2, -1, -1, 0, 8, 100000};
+    const int txcd[] = {-2, -1, -1, 0, 1, 7, 64, 1 << 29};
+    const int offs[] = {0, 0, 0, 0, 2, 1, 16, 8};
+    for (int i = 0; i < iters; ++i) {
+        const int W = pick(worlds, 12), T = pick(tokens, 14), H = pick(hiddens, 17);
+        const int maxw = 1 + (int)(next() % 16), maxt = (int)(next() % 20000), maxh = 1 + (int)(next() % 65536);
+        const int cu = (next() % 8) ? 256 : (int)(next() % 300);
+        arrms_tuning_t tun = {pick(tvpt, 8), pick(ttpr, 13), pick(tblk, 7), pick(tspl, 6), pick(txcd, 8)};
+        const arrms_tuning_t* tp = (next() % 3) ? &tun : nullptr;
+        const int variant = (int)(next() % 6) - 1;
+        const uintptr_t base = 0x7f0000000000ull;
+        const uintptr_t step = 1ull << 36;
+        const void* parts[17];
+        for (int r = 0; r < 17; ++r) parts[r] = (const void*)(base + r * step + pick(offs, 8));
+        const void* res = (const void*)(base + 20 * step + pick(offs, 8));
+        const void* w = (const void*)(base + 21 * step);
+        void* ro = (next() % 10) ? (void*)(base + 22 * step) : (void*)res;
+        void* no = (void*)(base + 23 * step + pick(offs, 8));
+        const float eps = (next() % 10) ? 1e-6f : -1.0f;
+        arrms_plan_t p;
+        const int rc = arrms_plan(cu, variant, tp, maxw, maxt, maxh, parts, W, T, H, res, w, eps, ro, no, &p);
+        if (rc == ARRMS_OK && T > 0 && p.grid > 0) {
+            if (p.blocks > p.grid || p.block < 64 || p.block > 1024 || p.block % 64) return fail("shape", i);
+            if (p.variant == ARRMS_VARIANT_ROW) {
+                if ((long)p.blocks * p.rows_per_block < T) return fail("row cover", i);
+                if ((long)p.threads_per_row * p.vec_per_thread < H / 8) return fail("row width", i);
+                if (p.block != p.threads_per_row * p.rows_per_block) return fail("row block", i);
+            } else if (p.variant == ARRMS_VARIANT_SPLITH) {
+                if ((long)p.chunks_per_row * p.block * p.vec_per_thread < H / 8) return fail("split cover", i);
+                if (p.blocks != T * p.chunks_per_row) return fail("split blocks", i);
+                if (p.chunks_per_row > (((maxh + 7) / 8 + 63) / 64)) return fail("workspace", i);
+            } else if (p.variant == ARRMS_VARIANT_SCALAR) {
+                if (p.grid != T) return fail("scalar grid", i);
+            } else {
+                return fail("variant", i);
+            }
+            if (p.xcd_chunk && p.grid % (8 * p.xcd_chunk)) return fail("xcd grid", i);
+        }
+        const int rc2 = arrms_plan_reduce(cu, tp, maxw, maxt, maxh, parts, W, T, H, no, &p);
+        if (rc2 == ARRMS_OK && T > 0 && p.grid > 0) {
+            const long long count = (long long)T * H;
+            if (p.variant == ARRMS_VARIANT_REDUCE) {
+                if ((long long)p.blocks * p.block * p.vec_per_thread < count / 8) return fail("reduce cover", i);
+            } else if (p.variant != ARRMS_VARIANT_REDUCE_SCALAR) {
+                return fail("reduce variant", i);
+            }
+        }
+    }
+    printf("plan fuzz ok: %d iterations\n", iters);
+    return 0;
+}

@@ -265,7 +265,7 @@ def test_reduce_plans_cover_every_element(W, T, H):
     nvec = T * H // 8
     per_block = p["block"] * p["vec_per_thread"]
     assert p["blocks"] == max(1, -(-nvec // per_block)) and p["grid"] == grid_of(p)
-    assert p["vec_per_thread"] == (4 if W <= 8 else 1)
+    assert p["vec_per_thread"] == 1
 
 
 def test_reduce_plan_validation():

@@ -1,0 +1,82 @@
+"""The fused call inside a captured HIP graph: replayed several times, with the
+program's own eager work and synchronisations between replays, every replay must
+equal the eager result bit for bit (the kernels use no memset nodes and the split-H
+workspace needs no reset between calls)."""
+import numpy as np
+import pytest
+import torch
+
+import residual_add_rmsnorm_arrms_amd as A
+import synth
+from tests.gpu_util import assert_parity, inputs, op, reference, say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0)
+
+
+@pytest.mark.parametrize("W,T,H,variant", [(4, 1, 2048, A.ARRMS_VARIANT_AUTO), (4, 16, 2048, A.ARRMS_VARIANT_AUTO),
+                                           (8, 1, 8192, A.ARRMS_VARIANT_AUTO), (4, 128, 2048, A.ARRMS_VARIANT_SPLITH),
+                                           (4, 300, 2048, A.ARRMS_VARIANT_ROW), (3, 5, 1001, A.ARRMS_VARIANT_AUTO)])
+def test_graph_replays_match_eager(W, T, H, variant):
+    say("case graph W=%d T=%d H=%d variant=%d" % (W, T, H, variant))
+    o = op()
+    o.set_variant(variant)
+    try:
+        cases = [inputs(W, T, H, seed=400 + i) for i in range(3)]
+        xd = torch.empty((W, T, H), dtype=torch.bfloat16, device=DEV)
+        rd = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+        wd = torch.empty((H,), dtype=torch.bfloat16, device=DEV)
+        ro = torch.empty_like(rd)
+        no = torch.empty_like(rd)
+        xd.copy_(cases[0][0].to(DEV)); rd.copy_(cases[0][1].to(DEV)); wd.copy_(cases[0][2].to(DEV))
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            o(xd, rd, wd, 1e-6, ro, no)   # warm-up outside capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            o(xd, rd, wd, 1e-6, ro, no)
+            o(xd, rd, wd, 1e-6, ro, no)   # two calls per replay: the second sees the first's workspace
+        for rep in range(6):
+            x, r, w = cases[rep % 3]
+            xd.copy_(x.to(DEV)); rd.copy_(r.to(DEV)); wd.copy_(w.to(DEV))
+            ro.fill_(0); no.fill_(0)         # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            got_ro, got_no = synth.bits(ro.cpu()), synth.bits(no.cpu())
+            eager_ro, eager_no = o(xd, rd, wd, 1e-6)
+            torch.cuda.synchronize()
+            assert np.array_equal(got_ro, synth.bits(eager_ro.cpu()))
+            assert np.array_equal(got_no, synth.bits(eager_no.cpu()))
+            assert_parity(got_ro, got_no, reference(x, r, w, 1e-6), "graph replay %d" % rep)
+        del g
+    finally:
+        o.set_variant(A.ARRMS_VARIANT_AUTO)
+
+
+def test_reduce_in_graph():
+    say("case graph reduce")
+    x, r, w = inputs(8, 64, 5120, seed=410)
+    xd = x.to(DEV)
+    out = torch.empty((64, 5120), dtype=torch.bfloat16, device=DEV)
+    o = op()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o.reduce(xd, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        o.reduce(xd, out)
+    want = reference(x, r, w, 1e-6)["reduced"]
+    for rep in range(4):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(synth.bits(out.cpu()), want)
+    del g

@@ -83,3 +83,21 @@ def test_two_stage_form_equals_fused(W, T, H):
     assert torch.equal(ro1.view(torch.int16), ro2.view(torch.int16))
     assert torch.equal(no1.view(torch.int16), no2.view(torch.int16))
     assert_parity(synth.bits(ro2.cpu()), synth.bits(no2.cpu()), reference(x, res, w, 1e-6), "two-stage")
+
+
+@pytest.mark.parametrize("W", [2, 4, 8, 12])
+@pytest.mark.parametrize("vpt", [1, 2, 4])
+@pytest.mark.parametrize("k", [0, 3, 64])
+def test_reduce_tunings(W, vpt, k):
+    """Every rank-sum kernel instance and XCD mapping, on a ragged element count."""
+    if W > 8 and vpt > 1:
+        pytest.skip("W > 8 has only the one-vector instance")
+    say("case reduce tuning W=%d vpt=%d K=%d" % (W, vpt, k))
+    x, res, w = inputs(W, 301, 1000, seed=310 + W)
+    o = op()
+    o.set_tuning(vec_per_thread=vpt, xcd_chunk=k)
+    try:
+        got = reduce_gpu(x)
+    finally:
+        o.set_tuning()
+    assert np.array_equal(got, reference(x, res, w, 1e-6)["reduced"])
