@@ -34,7 +34,9 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "achieved HBM GB/s (% of peak) and µs/call, W=4 H=2048 at T=1..4096"
 SWEEP_T = [1, 16, 64, 128, 256, 1024, 4096]
 POOL_SLOTS = 10
-KERNEL_SRC = os.path.join(ROOT, "residual_add_rmsnorm_arrms_amd", "csrc", "arrms_kernels.hip")
+# the fused kernels and the device helpers they include
+KERNEL_SRC = [os.path.join(ROOT, "residual_add_rmsnorm_arrms_amd", "csrc", f)
+              for f in ("arrms_device.h", "arrms_kernels.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_w4_h2048_t4096.json")
 
 
@@ -46,7 +48,7 @@ def kernel_source_hash() -> str:
     """Hash of the kernel source without comments and blank lines: what the counters were
     measured on (a comment edit leaves it unchanged, a code edit does not)."""
     import re
-    text = open(KERNEL_SRC).read()
+    text = "".join(open(f).read() for f in KERNEL_SRC)
     text = re.sub(r"//[^\n]*", "", text)
     code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
     return hashlib.sha256(code.encode()).hexdigest()[:16]

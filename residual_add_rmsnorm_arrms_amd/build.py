@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libarrms.so")
-SOURCES = [os.path.join(CSRC, "arrms_kernels.hip"), os.path.join(CSRC, "arrms_api.cpp")]
+SOURCES = [os.path.join(CSRC, "arrms_kernels.hip"), os.path.join(CSRC, "arrms_reduce.hip"),
+           os.path.join(CSRC, "arrms_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -1,0 +1,190 @@
+// Device helpers shared by the gfx950 kernels of the fused rank-partial sum +
+// residual add + RMSNorm (arrms_kernels.hip) and of the rank sum alone
+// (arrms_reduce.hip): BF16 conversion and rounding, streaming 16-byte memory
+// access, the XCD block mapping, cross-lane binary64 reductions and the
+// per-vector arithmetic of every step.  See arrms_kernels.hip for the
+// operation and its rounding points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "arrms_internal.h"
+
+namespace arrms {
+namespace dev {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- BF16 helpers
+// A dword holds two BF16 values: element 2i in the low half, 2i+1 in the high
+// half.  Widening is exact: the BF16 bits are the top half of a binary32.
+__device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// binary32 -> nearest BF16 value (ties to even), returned as a binary32 bit
+// pattern whose low 16 bits are zero.  Adding 0x7fff plus the lowest kept bit
+// carries into the kept half exactly when the dropped half exceeds one half,
+// or equals one half with an odd kept half.  A NaN keeps its top half with
+// the quiet bit set.
+__device__ __forceinline__ uint32_t round_bf16(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
+    const uint32_t quiet_nan = (u | 0x00400000u) & 0xffff0000u;
+    return __builtin_isnan(f) ? quiet_nan : rounded;
+}
+
+__device__ __forceinline__ uint32_t pack2(uint32_t lo_rounded, uint32_t hi_rounded) {
+    return (lo_rounded >> 16) | hi_rounded;
+}
+
+// 16-byte loads and stores.  The partials and the residual are read exactly
+// once, so they are loaded with the non-temporal (streaming) hint; the weight,
+// read by every row, is loaded normally so that it stays cached.  The outputs
+// are written once and not read again by this kernel: streaming stores.
+__device__ __forceinline__ u32x4 ld4(const void* base, size_t i) {
+    return static_cast<const u32x4*>(base)[i];
+}
+__device__ __forceinline__ u32x4 ld4_stream(const void* base, size_t i) {
+    return __builtin_nontemporal_load(static_cast<const u32x4*>(base) + i);
+}
+__device__ __forceinline__ void st4(void* base, size_t i, u32x4 v) { static_cast<u32x4*>(base)[i] = v; }
+__device__ __forceinline__ void st4_stream(void* base, size_t i, u32x4 v) {
+    __builtin_nontemporal_store(v, static_cast<u32x4*>(base) + i);
+}
+
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8).  With xcd_chunk = K > 0 the launched grid is a multiple of 8K and
+// the i-th workgroup an XCD receives takes logical block (8 * (i / K) + x) * K
+// + i % K (x = its XCD): runs of K consecutive blocks (rows) stay on one XCD,
+// and at any moment the 8 XCDs work on neighbouring runs.  K = 0 keeps the
+// hardware's round-robin order.  Returns -1 for padding blocks past a.blocks.
+__device__ __forceinline__ int logical_block(const Args& a) {
+    const int b = blockIdx.x;
+    const int k = a.xcd_chunk;
+    if (k == 0) return b;
+    const int x = b & 7;
+    const int i = b >> 3;
+    const int j = i / k;
+    const int l = (j * 8 + x) * k + (i - j * k);
+    return l < a.blocks ? l : -1;
+}
+
+// ---------------------------------------------------------------- reductions
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                          static_cast<uint32_t>(lo));
+}
+
+// Lane i reads lane i ^ 16 within each half-wave: ds_swizzle bit-mask mode,
+// and-mask 0x1f, or-mask 0, xor-mask 0x10.
+__device__ __forceinline__ double swizzle_xor16_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_ds_swizzle(static_cast<int>(b), 0x401F);
+    const int hi = __builtin_amdgcn_ds_swizzle(static_cast<int>(b >> 32), 0x401F);
+    return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                          static_cast<uint32_t>(lo));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), lane);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), lane);
+    return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                          static_cast<uint32_t>(lo));
+}
+
+// Sum of v over aligned groups of `width` lanes (16, 32 or 64); every lane of a
+// group receives the group's sum.  Butterfly order: lane ^ 1, ^ 2 (DPP quad
+// permutes), the other quad of each 8 (row_half_mirror), the other 8 of each 16
+// (row_mirror), the other 16 of each 32 (ds_swizzle), then the two half-waves
+// (readlane).  After each step a group's lanes hold equal values, so the mirror
+// permutes act as xor partners, and binary64 addition being commutative gives
+// every lane bit-identical sums.  The order is fixed, so results are
+// deterministic; they can differ from a sequential sum in the last binary64
+// bit, which changes the binary32 1/RMS only when the exact value lies within
+// about 2^-29 relative of a binary32 rounding boundary.  Needs all 64 lanes
+// active.
+__device__ __forceinline__ double seg_sum(double v, int width) {
+    v = v + dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = v + dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = v + dpp_f64<0x141>(v);  // row_half_mirror
+    v = v + dpp_f64<0x140>(v);  // row_mirror
+    if (width >= 32) v = v + swizzle_xor16_f64(v);
+    if (width >= 64) v = readlane_f64(v, 0) + readlane_f64(v, 32);
+    return v;
+}
+
+// 1 / RMS of a row from its binary64 sum of squares.
+__device__ __forceinline__ float inv_rms(double sum_sq, double hidden, float eps) {
+    return static_cast<float>(1.0 / sqrt(sum_sq / hidden + static_cast<double>(eps)));
+}
+
+// ------------------------------------------------------- per-vector arithmetic
+// Rank sum, reduced rounding and residual add for one 16-byte vector (8
+// elements) of a row; accumulates the squares into ss and returns residual_out.
+// binary32 rank sum, in rank order from x_0, of the two elements in dword j.
+template <int W>
+__device__ __forceinline__ void rank_sum(const u32x4 (&xv)[W > 0 ? W : kMaxWorld], int world, int j, float& a_lo,
+                                         float& a_hi) {
+    constexpr int WA = W > 0 ? W : kMaxWorld;
+    a_lo = lo_f32(xv[0][j]);
+    a_hi = hi_f32(xv[0][j]);
+#pragma unroll
+    for (int r = 1; r < WA; ++r) {
+        if (W > 0 || r < world) {
+            a_lo = a_lo + lo_f32(xv[r][j]);
+            a_hi = a_hi + hi_f32(xv[r][j]);
+        }
+    }
+}
+
+// `reduced` for one vector: the rank sum rounded to BF16.
+template <int W>
+__device__ __forceinline__ u32x4 reduced_vec(const u32x4 (&xv)[W > 0 ? W : kMaxWorld], int world) {
+    u32x4 out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float a_lo, a_hi;
+        rank_sum<W>(xv, world, j, a_lo, a_hi);
+        out[j] = pack2(round_bf16(a_lo), round_bf16(a_hi));
+    }
+    return out;
+}
+
+template <int W>
+__device__ __forceinline__ u32x4 residual_vec(const u32x4 (&xv)[W > 0 ? W : kMaxWorld], int world,
+                                              u32x4 rv, double& ss) {
+    u32x4 ro;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float a_lo, a_hi;
+        rank_sum<W>(xv, world, j, a_lo, a_hi);
+        const uint32_t o_lo = round_bf16(__uint_as_float(round_bf16(a_lo)) + lo_f32(rv[j]));
+        const uint32_t o_hi = round_bf16(__uint_as_float(round_bf16(a_hi)) + hi_f32(rv[j]));
+        const double d_lo = static_cast<double>(__uint_as_float(o_lo));
+        const double d_hi = static_cast<double>(__uint_as_float(o_hi));
+        ss = ss + d_lo * d_lo;  // exact square of a BF16 value in binary64
+        ss = ss + d_hi * d_hi;
+        ro[j] = pack2(o_lo, o_hi);
+    }
+    return ro;
+}
+
+// norm_out for one vector from residual_out, 1/RMS and the weight.
+__device__ __forceinline__ u32x4 norm_vec(u32x4 ro, float inv, u32x4 wv) {
+    u32x4 out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float n_lo = (lo_f32(ro[j]) * inv) * lo_f32(wv[j]);
+        const float n_hi = (hi_f32(ro[j]) * inv) * hi_f32(wv[j]);
+        out[j] = pack2(round_bf16(n_lo), round_bf16(n_hi));
+    }
+    return out;
+}
+
+}  // namespace dev
+}  // namespace arrms

@@ -1,0 +1,104 @@
+// gfx950 kernels of the rank sum alone: reduced = BF16(sum over the W rank
+// partials), the first line of the contract of the page "[TLERaw] Add NVSHMEM
+// allreduce RMSNorm tutorial" (FlagTree PR #1122, section Summary), i.e. the
+// page's collective stage (section Implementation 1) on one GPU's share.  Same
+// arithmetic as the fused kernels: binary32 sum in rank order from x_0, one
+// rounding to BF16.  Bound by HBM bandwidth: 2 * (W + 1) bytes per element.
+#include <hip/hip_runtime.h>
+
+#include "arrms_device.h"
+
+namespace arrms {
+namespace {
+
+using namespace dev;
+
+hipError_t launch(const void* fn, const Args& a, int grid, int block, hipStream_t s) {
+    void* args[] = {const_cast<Args*>(&a)};
+    return hipLaunchKernel(fn, dim3(grid), dim3(block), args, 0, s);
+}
+
+// ------------------------------------------------------------ rank sum only
+// The contract's first line on its own (the page's collective stage, locally):
+// reduced = BF16(sum of the W partials), flat over a.count = T*H elements.
+// Each lane sums VPT 16-byte vectors (at stride blockDim) of every partial;
+// the last count % 8 elements go element-wise in the last block.
+template <int W, int kReduceVpt>
+__global__ void __launch_bounds__(256) reduce_kernel(const Args a) {
+    constexpr int WA = W > 0 ? W : kMaxWorld;
+    const int world = W > 0 ? W : a.world;
+    const int block = logical_block(a);
+    if (block < 0) return;
+    const size_t nvec = static_cast<size_t>(a.count) / 8;
+    const size_t first = static_cast<size_t>(block) * blockDim.x * kReduceVpt + threadIdx.x;
+    bool ok[kReduceVpt];
+    u32x4 xv[kReduceVpt][WA];
+#pragma unroll
+    for (int k = 0; k < kReduceVpt; ++k) {
+        const size_t v = first + static_cast<size_t>(k) * blockDim.x;
+        ok[k] = v < nvec;
+        if (ok[k]) {
+#pragma unroll
+            for (int r = 0; r < WA; ++r)
+                if (W > 0 || r < world) xv[k][r] = ld4_stream(a.x.p[r], v);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kReduceVpt; ++k)
+        if (ok[k]) st4_stream(a.reduced, first + static_cast<size_t>(k) * blockDim.x, reduced_vec<W>(xv[k], world));
+    if (block == a.blocks - 1) {  // the count % 8 elements past the last whole vector
+        for (size_t e = nvec * 8 + threadIdx.x; e < static_cast<size_t>(a.count); e += blockDim.x) {
+            float acc = lo_f32(static_cast<const uint16_t*>(a.x.p[0])[e]);
+            for (int r = 1; r < world; ++r) acc = acc + lo_f32(static_cast<const uint16_t*>(a.x.p[r])[e]);
+            static_cast<uint16_t*>(a.reduced)[e] = static_cast<uint16_t>(round_bf16(acc) >> 16);
+        }
+    }
+}
+
+// Rank sum only, element-wise, for pointers that are not 16-byte aligned.
+__global__ void __launch_bounds__(256) reduce_scalar_kernel(const Args a) {
+    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+    for (size_t e = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < static_cast<size_t>(a.count);
+         e += stride) {
+        float acc = lo_f32(static_cast<const uint16_t*>(a.x.p[0])[e]);
+        for (int r = 1; r < a.world; ++r) acc = acc + lo_f32(static_cast<const uint16_t*>(a.x.p[r])[e]);
+        static_cast<uint16_t*>(a.reduced)[e] = static_cast<uint16_t>(round_bf16(acc) >> 16);
+    }
+}
+
+template <int VPT>
+const void* reduce_fn(int world) {
+    switch (world) {
+        case 1: return reinterpret_cast<const void*>(&reduce_kernel<1, VPT>);
+        case 2: return reinterpret_cast<const void*>(&reduce_kernel<2, VPT>);
+        case 3: return reinterpret_cast<const void*>(&reduce_kernel<3, VPT>);
+        case 4: return reinterpret_cast<const void*>(&reduce_kernel<4, VPT>);
+        case 5: return reinterpret_cast<const void*>(&reduce_kernel<5, VPT>);
+        case 6: return reinterpret_cast<const void*>(&reduce_kernel<6, VPT>);
+        case 7: return reinterpret_cast<const void*>(&reduce_kernel<7, VPT>);
+        case 8: return reinterpret_cast<const void*>(&reduce_kernel<8, VPT>);
+        default: break;
+    }
+    if constexpr (VPT == 1) return reinterpret_cast<const void*>(&reduce_kernel<0, 1>);
+    return nullptr;
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const Args& a, int vpt, int grid, int block, hipStream_t s) {
+    const void* fn = nullptr;
+    switch (vpt) {
+        case 1: fn = reduce_fn<1>(a.world); break;
+        case 2: fn = reduce_fn<2>(a.world); break;
+        case 4: fn = reduce_fn<4>(a.world); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (!fn) return hipErrorInvalidValue;
+    return launch(fn, a, grid, block, s);
+}
+
+hipError_t launch_reduce_scalar(const Args& a, int grid, int block, hipStream_t s) {
+    return launch(reinterpret_cast<const void*>(&reduce_scalar_kernel), a, grid, block, s);
+}
+
+}  // namespace arrms
