@@ -88,6 +88,7 @@ typedef struct {
     int splith_block;      /* split-H: threads per workgroup, 64..1024, multiple of 64 */
     int splith_max_tokens; /* automatic variant uses split-H when tokens <= this; -1 automatic */
     int xcd_chunk;         /* -1 automatic; 0 hardware round-robin; K > 0 runs of K blocks per XCD */
+    int rows_per_block;    /* row: token rows per workgroup (power of two); 0 automatic */
 } arrms_tuning_t;
 
 /*

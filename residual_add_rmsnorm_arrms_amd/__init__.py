@@ -56,11 +56,12 @@ class arrms_plan_t(ctypes.Structure):
 
 class arrms_tuning_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("vec_per_thread", "threads_per_row", "splith_block",
-                                            "splith_max_tokens", "xcd_chunk")]
+                                            "splith_max_tokens", "xcd_chunk", "rows_per_block")]
 
     @classmethod
-    def make(cls, vec_per_thread=0, threads_per_row=0, splith_block=0, splith_max_tokens=-1, xcd_chunk=-1):
-        return cls(vec_per_thread, threads_per_row, splith_block, splith_max_tokens, xcd_chunk)
+    def make(cls, vec_per_thread=0, threads_per_row=0, splith_block=0, splith_max_tokens=-1, xcd_chunk=-1,
+             rows_per_block=0):
+        return cls(vec_per_thread, threads_per_row, splith_block, splith_max_tokens, xcd_chunk, rows_per_block)
 
 
 class ArrmsError(RuntimeError):

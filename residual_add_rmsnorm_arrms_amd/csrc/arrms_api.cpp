@@ -84,6 +84,8 @@ bool valid_tuning(const arrms_tuning_t* t) {
     if (!(b == 0 || (b > 0 && b % 64 == 0 && b <= 1024))) return false;
     if (t->splith_max_tokens < -1) return false;
     if (t->xcd_chunk < -1) return false;
+    const int rp = t->rows_per_block;
+    if (rp < 0 || rp > 64 || (rp & (rp - 1))) return false;
     return true;
 }
 
@@ -127,6 +129,10 @@ int plan_row(int world, int tokens, int hidden, const arrms_tuning_t* t, arrms_p
     if (!best_vpt) return ARRMS_ERR_UNSUPPORTED;
     int rpb = best_tpr < 256 ? 256 / best_tpr : 1;
     while (rpb > 1 && best_tpr * rpb > row_max_threads(world, best_vpt)) rpb /= 2;
+    if (t && t->rows_per_block) {
+        rpb = t->rows_per_block;
+        if (best_tpr * rpb > row_max_threads(world, best_vpt) || (best_tpr * rpb) % 64) return ARRMS_ERR_UNSUPPORTED;
+    }
     p->variant = ARRMS_VARIANT_ROW;
     p->vec_per_thread = best_vpt;
     p->threads_per_row = best_tpr;

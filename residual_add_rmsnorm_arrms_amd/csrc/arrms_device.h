@@ -21,21 +21,19 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// binary32 -> nearest BF16 value (ties to even), returned as a binary32 bit
-// pattern whose low 16 bits are zero.  Adding 0x7fff plus the lowest kept bit
-// carries into the kept half exactly when the dropped half exceeds one half,
-// or equals one half with an odd kept half.  A NaN keeps its top half with
-// the quiet bit set.
-__device__ __forceinline__ uint32_t round_bf16(float f) {
-    const uint32_t u = __float_as_uint(f);
-    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
-    const uint32_t quiet_nan = (u | 0x00400000u) & 0xffff0000u;
-    return __builtin_isnan(f) ? quiet_nan : rounded;
+// binary32 -> BF16, round to nearest, ties to even: gfx950's packed
+// conversion (v_cvt_pk_bf16_f32) under the default rounding mode, with binary32
+// denormals preserved (the kernels are built without flush-to-zero).  A carry
+// out of the largest finite values gives infinity; a NaN stays a NaN (its
+// payload is the hardware's).  cvt2 packs two results into one dword, the
+// first in the low half; cvt1 returns one BF16 bit pattern.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt2(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
-
-__device__ __forceinline__ uint32_t pack2(uint32_t lo_rounded, uint32_t hi_rounded) {
-    return (lo_rounded >> 16) | hi_rounded;
-}
+__device__ __forceinline__ uint16_t cvt1(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 
 // 16-byte loads and stores.  The partials and the residual are read exactly
 // once, so they are loaded with the non-temporal (streaming) hint; the weight,
@@ -150,7 +148,7 @@ __device__ __forceinline__ u32x4 reduced_vec(const u32x4 (&xv)[W > 0 ? W : kMaxW
     for (int j = 0; j < 4; ++j) {
         float a_lo, a_hi;
         rank_sum<W>(xv, world, j, a_lo, a_hi);
-        out[j] = pack2(round_bf16(a_lo), round_bf16(a_hi));
+        out[j] = cvt2(a_lo, a_hi);
     }
     return out;
 }
@@ -163,13 +161,15 @@ __device__ __forceinline__ u32x4 residual_vec(const u32x4 (&xv)[W > 0 ? W : kMax
     for (int j = 0; j < 4; ++j) {
         float a_lo, a_hi;
         rank_sum<W>(xv, world, j, a_lo, a_hi);
-        const uint32_t o_lo = round_bf16(__uint_as_float(round_bf16(a_lo)) + lo_f32(rv[j]));
-        const uint32_t o_hi = round_bf16(__uint_as_float(round_bf16(a_hi)) + hi_f32(rv[j]));
-        const double d_lo = static_cast<double>(__uint_as_float(o_lo));
-        const double d_hi = static_cast<double>(__uint_as_float(o_hi));
-        ss = ss + d_lo * d_lo;  // exact square of a BF16 value in binary64
-        ss = ss + d_hi * d_hi;
-        ro[j] = pack2(o_lo, o_hi);
+        const uint32_t red = cvt2(a_lo, a_hi);
+        const uint32_t o = cvt2(lo_f32(red) + lo_f32(rv[j]), hi_f32(red) + hi_f32(rv[j]));
+        const double d_lo = static_cast<double>(lo_f32(o));
+        const double d_hi = static_cast<double>(hi_f32(o));
+        // The square of a BF16 value is exact in binary64, so the fused
+        // multiply-add rounds once, exactly as square-then-add does.
+        ss = __builtin_fma(d_lo, d_lo, ss);
+        ss = __builtin_fma(d_hi, d_hi, ss);
+        ro[j] = o;
     }
     return ro;
 }
@@ -181,7 +181,7 @@ __device__ __forceinline__ u32x4 norm_vec(u32x4 ro, float inv, u32x4 wv) {
     for (int j = 0; j < 4; ++j) {
         const float n_lo = (lo_f32(ro[j]) * inv) * lo_f32(wv[j]);
         const float n_hi = (hi_f32(ro[j]) * inv) * hi_f32(wv[j]);
-        out[j] = pack2(round_bf16(n_lo), round_bf16(n_hi));
+        out[j] = cvt2(n_lo, n_hi);
     }
     return out;
 }

@@ -204,10 +204,10 @@ __global__ void __launch_bounds__(256) scalar_kernel(const Args a) {
     for (int h = tid; h < H; h += nthreads) {
         float acc = lo_f32(static_cast<const uint16_t*>(a.x.p[0])[base + h]);
         for (int r = 1; r < a.world; ++r) acc = acc + lo_f32(static_cast<const uint16_t*>(a.x.p[r])[base + h]);
-        const uint32_t o = round_bf16(__uint_as_float(round_bf16(acc)) + lo_f32(res[base + h]));
-        ro_out[base + h] = static_cast<uint16_t>(o >> 16);
-        const double d = static_cast<double>(__uint_as_float(o));
-        ss = ss + d * d;
+        const uint16_t o = cvt1(lo_f32(cvt1(acc)) + lo_f32(res[base + h]));
+        ro_out[base + h] = o;
+        const double d = static_cast<double>(lo_f32(o));
+        ss = __builtin_fma(d, d, ss);
     }
     __shared__ double wave_ss[4];
     ss = seg_sum(ss, 64);
@@ -218,7 +218,7 @@ __global__ void __launch_bounds__(256) scalar_kernel(const Args a) {
     const float inv = inv_rms(total, a.hidden_d, a.eps);
     for (int h = tid; h < H; h += nthreads) {
         const float n = (lo_f32(ro_out[base + h]) * inv) * lo_f32(w[h]);
-        n_out[base + h] = static_cast<uint16_t>(round_bf16(n) >> 16);
+        n_out[base + h] = cvt1(n);
     }
 }
 

@@ -50,7 +50,7 @@ __global__ void __launch_bounds__(256) reduce_kernel(const Args a) {
         for (size_t e = nvec * 8 + threadIdx.x; e < static_cast<size_t>(a.count); e += blockDim.x) {
             float acc = lo_f32(static_cast<const uint16_t*>(a.x.p[0])[e]);
             for (int r = 1; r < world; ++r) acc = acc + lo_f32(static_cast<const uint16_t*>(a.x.p[r])[e]);
-            static_cast<uint16_t*>(a.reduced)[e] = static_cast<uint16_t>(round_bf16(acc) >> 16);
+            static_cast<uint16_t*>(a.reduced)[e] = cvt1(acc);
         }
     }
 }
@@ -62,7 +62,7 @@ __global__ void __launch_bounds__(256) reduce_scalar_kernel(const Args a) {
          e += stride) {
         float acc = lo_f32(static_cast<const uint16_t*>(a.x.p[0])[e]);
         for (int r = 1; r < a.world; ++r) acc = acc + lo_f32(static_cast<const uint16_t*>(a.x.p[r])[e]);
-        static_cast<uint16_t*>(a.reduced)[e] = static_cast<uint16_t>(round_bf16(acc) >> 16);
+        static_cast<uint16_t*>(a.reduced)[e] = cvt1(acc);
     }
 }
 

@@ -47,7 +47,8 @@ int main(int argc, char** argv) {
         const int W = pick(worlds, 12), T = pick(tokens, 14), H = pick(hiddens, 17);
         const int maxw = 1 + (int)(next() % 16), maxt = (int)(next() % 20000), maxh = 1 + (int)(next() % 65536);
         const int cu = (next() % 8) ? 256 : (int)(next() % 300);
-        arrms_tuning_t tun = {pick(tvpt, 8), pick(ttpr, 13), pick(tblk, 7), pick(tspl, 6), pick(txcd, 8)};
+        const int trpb[] = {0, 0, 0, 1, 2, 3, 4, 8, 64, 128};
+        arrms_tuning_t tun = {pick(tvpt, 8), pick(ttpr, 13), pick(tblk, 7), pick(tspl, 6), pick(txcd, 8), pick(trpb, 10)};
         const arrms_tuning_t* tp = (next() % 3) ? &tun : nullptr;
         const int variant = (int)(next() % 6) - 1;
         const uintptr_t base = 0x7f0000000000ull;

@@ -209,8 +209,9 @@ def test_aliasing_rules():
     assert plan(4, 16, 2048, partials=[p[0], p[0], p[0], p[0]])[0] == A.ARRMS_OK
 
 
-@pytest.mark.parametrize("t", [(3, 0, 0, -1, -1), (0, 48, 0, -1, -1), (0, 2048, 0, -1, -1),
-                               (0, 0, 100, -1, -1), (0, 0, 0, -2, -1), (0, 0, 0, -1, -2)])
+@pytest.mark.parametrize("t", [(3, 0, 0, -1, -1, 0), (0, 48, 0, -1, -1, 0), (0, 2048, 0, -1, -1, 0),
+                               (0, 0, 100, -1, -1, 0), (0, 0, 0, -2, -1, 0), (0, 0, 0, -1, -2, 0),
+                               (0, 0, 0, -1, -1, 3), (0, 0, 0, -1, -1, -1), (0, 0, 0, -1, -1, 128)])
 def test_invalid_tuning(t):
     assert plan(4, 16, 2048, tuning=A.arrms_tuning_t(*t))[0] == A.ARRMS_ERR_INVALID_ARG
 
@@ -280,3 +281,10 @@ def test_reduce_plan_validation():
     rc, p = A.arrms_plan_reduce(CU, None, 4, 10, 2048, None, 4, 0, 2048, 0)
     assert rc == A.ARRMS_OK and p["grid"] == 0
     assert A.arrms_reduce(None, b["partials"], 4, 16, 2048, b["residual_out"], 0) == A.ARRMS_ERR_INVALID_ARG
+
+
+def test_rows_per_block_tuning():
+    rc, p = plan(4, 4096, 2048, tuning=A.arrms_tuning_t.make(rows_per_block=4))
+    assert rc == A.ARRMS_OK and p["rows_per_block"] == 4 and p["block"] == 1024 and p["blocks"] == 1024
+    rc, p = plan(4, 4096, 2048, variant=A.ARRMS_VARIANT_ROW, tuning=A.arrms_tuning_t.make(rows_per_block=8))
+    assert rc == A.ARRMS_ERR_UNSUPPORTED                      # 2048 threads per workgroup
