@@ -288,3 +288,23 @@ def test_rows_per_block_tuning():
     assert rc == A.ARRMS_OK and p["rows_per_block"] == 4 and p["block"] == 1024 and p["blocks"] == 1024
     rc, p = plan(4, 4096, 2048, variant=A.ARRMS_VARIANT_ROW, tuning=A.arrms_tuning_t.make(rows_per_block=8))
     assert rc == A.ARRMS_ERR_UNSUPPORTED                      # 2048 threads per workgroup
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """No fallback: with the library missing every entry point raises."""
+    import subprocess
+    import sys
+    code = ("import residual_add_rmsnorm_arrms_amd as A; A.LIB_PATH = %r\n"
+            "try:\n    A.arrms_status_string(0)\nexcept RuntimeError as e:\n    print('raised', 'not built' in str(e))\n"
+            % str(tmp_path / "missing.so"))
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.check_output([sys.executable, "-c", code], cwd=root, env=dict(os.environ, PYTHONPATH=root))
+    assert out.decode().strip() == "raised True"
+
+
+def test_operator_checks_tensor_arguments():
+    import torch
+    op = A.FusedReduceResidualRMSNorm.__new__(A.FusedReduceResidualRMSNorm)  # no handle needed for the checks
+    x = torch.zeros((2, 4, 16), dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        op._args(x, torch.zeros((4, 16), dtype=torch.bfloat16), torch.zeros(16, dtype=torch.bfloat16), None, None)

@@ -311,3 +311,22 @@ def test_create_destroy_cycles():
     # the failed allocation leaves no stale error behind for the next launch check
     torch.zeros(1000, device="cuda").add_(1)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,variant", [("row", ROW), ("splith", SPLITH), ("scalar", SCALAR)])
+def test_force_variant_environment(name, variant, monkeypatch):
+    """ARRMS_FORCE_VARIANT is read once, when a handle is created."""
+    say("case ARRMS_FORCE_VARIANT=%s" % name)
+    monkeypatch.setenv("ARRMS_FORCE_VARIANT", name)
+    o = A.FusedReduceResidualRMSNorm(4, 64, 2048, device=0)
+    monkeypatch.delenv("ARRMS_FORCE_VARIANT")
+    try:
+        x, res, w = inputs(4, 40, 2048, seed=500)
+        dev = torch.device("cuda", 0)
+        xd, rd, wd = x.to(dev), res.to(dev), w.to(dev)
+        assert o.plan(xd, rd, wd, 1e-6)["variant"] == variant
+        ro, no = o(xd, rd, wd, 1e-6)
+        torch.cuda.synchronize()
+        assert_parity(synth.bits(ro.cpu()), synth.bits(no.cpu()), reference(x, res, w, 1e-6), "env " + name)
+    finally:
+        o.close()
