@@ -29,7 +29,7 @@ FLAGS = [
 def build(verbose: bool = False) -> str:
     """Compile the library (always, even when one exists) and return its path."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, "-Wl,-soname,libarrms.so", "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
