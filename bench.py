@@ -221,6 +221,31 @@ def time_graph(torch, call, calls_per_graph, replays):
     return ms
 
 
+def launch_floor_graph_us(torch, calls=100, replays=10):
+    """GPU time per launch of a one-element kernel replayed from a HIP graph: the floor
+    under any kernel's decode latency on this GPU (context for the T=1 sweep point)."""
+    t = torch.zeros(1, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        t.add_(1)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            t.add_(1)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (calls * replays)
+
+
 def pct(xs, q):
     xs = sorted(xs)
     return xs[min(len(xs) - 1, max(0, int(round(q / 100.0 * (len(xs) - 1)))))]
@@ -437,6 +462,8 @@ def main():
                 log("reduce only W=%d T=%5d: %.2f us, %.0f GB/s" % (w_, t, ms * 1e3, b / (ms * 1e-3) / 1e9))
         del red_pool
 
+    floor_us = launch_floor_graph_us(torch)
+    log("launch floor (one-element kernel, graph replay): %.2f us" % floor_us)
     copy = copy_context(torch, 512 * 2 ** 20)
     log("copy context: %.1f GB/s" % copy["GB_s"])
     tr = traffic_record()
@@ -475,6 +502,7 @@ def main():
         "fusion": fusion,
         "reduce_only": reduce_sweep,
         "copy_context": copy,
+        "launch_floor_graph_us": floor_us,
         "device": {"name": props.name, "compute_units": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", None), "memory_GiB": props.total_memory / 2 ** 30},
         "kernel_source_sha256_16": kernel_source_hash(),

@@ -180,6 +180,24 @@ def arrms_plan_reduce(cu_count: int, tuning: Optional[arrms_tuning_t], max_world
 
 
 # ---------------------------------------------------------------- torch-facing operator
+class BoundCall:
+    """arrms_fused on buffers fixed at bind time (see FusedReduceResidualRMSNorm.bind)."""
+
+    def __init__(self, owner, keep_alive, args, outputs):
+        self._owner = owner
+        self._keep = keep_alive
+        self._args = args
+        self._fn = load().arrms_fused
+        self.outputs = outputs
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != ARRMS_OK:
+            raise ArrmsError(rc, "arrms_fused")
+        return self.outputs
+
+
+
 class FusedReduceResidualRMSNorm:
     """Reusable operator over one handle.  Tensors: BF16, on the handle's GPU.
 
@@ -252,6 +270,26 @@ class FusedReduceResidualRMSNorm:
         if rc != ARRMS_OK:
             raise ArrmsError(rc, "arrms_fused")
         return residual_out, norm_out
+
+    def bind(self, partials, residual, weight, eps: float, residual_out=None, norm_out=None, stream=None):
+        """A prepared call on fixed buffers: the tensors are checked and the C arguments
+        marshalled once, and each call of the returned object only enqueues the kernel(s)
+        (for serving loops on static buffers).  The tensors must stay alive and in place;
+        the stream is fixed at bind time (torch's current stream by default)."""
+        import torch
+        parts, T, H, residual_out, norm_out = self._args(partials, residual, weight, residual_out, norm_out)
+        s = (stream if stream is not None else torch.cuda.current_stream(self.device)).cuda_stream
+        ptrs = [q.data_ptr() for q in parts]
+        rc, _ = arrms_query_plan(self.handle, ptrs, len(parts), T, H, residual.data_ptr(), weight.data_ptr(), eps,
+                                 residual_out.data_ptr(), norm_out.data_ptr())
+        if rc != ARRMS_OK:
+            raise ArrmsError(rc, "arrms_fused")
+        return BoundCall(self, (parts, residual, weight, residual_out, norm_out),
+                         (ctypes.c_void_p(self.handle), _ptrs(ptrs), len(parts), T, H,
+                          ctypes.c_void_p(residual.data_ptr()), ctypes.c_void_p(weight.data_ptr()),
+                          ctypes.c_float(eps), ctypes.c_void_p(residual_out.data_ptr()),
+                          ctypes.c_void_p(norm_out.data_ptr()), ctypes.c_void_p(s)),
+                         (residual_out, norm_out))
 
     def reduce(self, partials, reduced=None, stream=None):
         """reduced = BF16 rank sum of the partials ([W, T, H] or W x [T, H]); returns reduced."""

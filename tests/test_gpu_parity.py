@@ -330,3 +330,18 @@ def test_force_variant_environment(name, variant, monkeypatch):
         assert_parity(synth.bits(ro.cpu()), synth.bits(no.cpu()), reference(x, res, w, 1e-6), "env " + name)
     finally:
         o.close()
+
+
+def test_bound_call_matches_plain_call():
+    say("case bound call")
+    dev = torch.device("cuda", 0)
+    x, res, w = inputs(4, 77, 2048, seed=600)
+    xd, rd, wd = x.to(dev), res.to(dev), w.to(dev)
+    o = op()
+    call = o.bind(xd, rd, wd, 1e-6)
+    ro, no = call()
+    call()  # idempotent: same inputs, same outputs
+    torch.cuda.synchronize()
+    assert_parity(synth.bits(ro.cpu()), synth.bits(no.cpu()), reference(x, res, w, 1e-6), "bound call")
+    with pytest.raises(A.ArrmsError):
+        o.bind(xd, rd, wd, -1.0)
