@@ -52,7 +52,7 @@ def test_full_size_workload(name):
 
 
 # ------------------------------------------------------------ sweeps
-TOKENS = [1, 2, 3, 15, 16, 17, 63, 64, 127, 128, 255, 256, 257, 1024, 4096]
+TOKENS = [1, 2, 3, 15, 16, 17, 63, 64, 127, 128, 255, 256, 257, 1024, 4096, 16383]
 
 
 @pytest.mark.parametrize("T", TOKENS)
