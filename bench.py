@@ -9,9 +9,11 @@ partials and the residual, write residual_out and norm_out, read the weight once
 per call, divided by the time per call; also reported as a fraction of the 8 TB/s
 HBM3E peak, and as microseconds per call for T = 1, 16, 64, 128, 256, 1024, 4096.
 
-Inputs are resident in HBM before timing starts.  Calls walk through a 1.1 GiB
-pool of distinct input/output sets (more than twice the 256 MB Infinity Cache),
-so repeated calls cannot be served from cache.
+Inputs are resident in HBM before timing starts.  Calls walk through a 4.4 GiB
+pool of distinct input/output sets (10 slots of 16384 rows; far more than the
+256 MB Infinity Cache), so repeated calls cannot be served from cache.  Points at
+T = 4096, 8192, 16384 (beyond the metric's range) separate the per-call fixed time
+from the kernel's streaming rate.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -33,6 +35,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "achieved HBM GB/s (% of peak) and µs/call, W=4 H=2048 at T=1..4096"
 SWEEP_T = [1, 16, 64, 128, 256, 1024, 4096]
+# Beyond the metric's range, to separate the per-call fixed time from the streaming rate.
+FIT_T = [4096, 8192, 16384]
+POOL_ROWS = 16384
 POOL_SLOTS = 10
 # the fused kernels and the device helpers they include
 KERNEL_SRC = [os.path.join(ROOT, "residual_add_rmsnorm_arrms_amd", "csrc", f)
@@ -60,17 +65,23 @@ def algorithmic_bytes(W, T, H):
 
 class Pool:
     """POOL_SLOTS slots, each holding W partials, residual, residual_out and norm_out of
-    [T_max, H] BF16 in one device allocation.  A call with T rows uses rows
-    [j*T, (j+1)*T) of one slot, so successive calls touch fresh memory."""
+    [rows, H] BF16 in one device allocation (the input rows repeated to fill `rows`).
+    A call with T rows uses rows [j*T, (j+1)*T) of one slot, so successive calls touch
+    fresh memory."""
 
-    def __init__(self, torch, x, res, w):
-        W, T, H = x.shape
+    def __init__(self, torch, x, res, w, rows=None):
+        W, T_in, H = x.shape
+        T = rows or T_in
         self.W, self.T, self.H = W, T, H
         dev = torch.device("cuda", 0)
         self.tensor_elems = T * H
         self.slot = torch.empty((POOL_SLOTS, W + 3, T, H), dtype=torch.bfloat16, device=dev)
-        self.slot[0, :W].copy_(x.to(dev))
-        self.slot[0, W].copy_(res.to(dev))
+        xd, rd = x.to(dev), res.to(dev)
+        for r0 in range(0, T, T_in):
+            n = min(T_in, T - r0)
+            self.slot[0, :W, r0:r0 + n].copy_(xd[:, :n])
+            self.slot[0, W, r0:r0 + n].copy_(rd[:n])
+        del xd, rd
         for s in range(1, POOL_SLOTS):
             self.slot[s, :W + 1].copy_(self.slot[0, :W + 1])
         self.weight = w.to(dev)
@@ -81,9 +92,14 @@ class Pool:
     def nbytes(self):
         return self.slot.numel() * 2
 
-    def sets(self, T):
-        """Pointer sets (partials, residual, residual_out, norm_out) for T-row calls."""
-        per_slot = self.T // T
+    def reduced_ptr(self, base, T, j, s):
+        """Address of the reduced-output rows of set (j, s) in a [POOL_SLOTS, rows, H] buffer."""
+        return base + s * self.tensor_elems * 2 + j * T * self.H * 2
+
+    def sets(self, T, max_sets=8192):
+        """Pointer sets (partials, residual, residual_out, norm_out) for T-row calls: up to
+        max_sets distinct ones, cycling through the slots first."""
+        per_slot = min(self.T // T, max(1, max_sets // POOL_SLOTS))
         out = []
         for j in range(per_slot):
             for s in range(POOL_SLOTS):
@@ -102,7 +118,7 @@ class ReduceCaller:
         lib = A.load()
         self.fn = lib.arrms_reduce
         vp = ctypes.c_void_p
-        per_slot = pool.T // T
+        per_slot = min(pool.T // T, max(1, 8192 // POOL_SLOTS))
         inputs_per_slot = pool.W + 1
         self.args = []
         te = pool.tensor_elems * 2
@@ -112,7 +128,7 @@ class ReduceCaller:
                 for r in range(W):
                     slot = (s + r // inputs_per_slot) % POOL_SLOTS
                     parts.append(pool.base + slot * (pool.W + 3) * te + (r % inputs_per_slot) * te + j * T * pool.H * 2)
-                out = out_base + s * te + j * T * pool.H * 2
+                out = pool.reduced_ptr(out_base, T, j, s)
                 self.args.append((vp(handle), (vp * W)(*parts), W, T, pool.H, vp(out)))
         self.stream = vp(stream)
         self.i = 0
@@ -350,9 +366,9 @@ def main():
     W, T, H, eps = wl.world, wl.tokens, wl.hidden, wl.eps
     log("generating inputs W=%d T=%d H=%d" % (W, T, H))
     x, res, w = synth.make_inputs(wl)
-    pool = Pool(torch, x, res, w)
+    pool = Pool(torch, x, res, w, rows=POOL_ROWS)
     log("pool: %d slots, %.2f GiB" % (POOL_SLOTS, pool.nbytes / 2 ** 30))
-    op = A.FusedReduceResidualRMSNorm(max_world=8, max_tokens=T, max_hidden=H, device=0)
+    op = A.FusedReduceResidualRMSNorm(max_world=8, max_tokens=POOL_ROWS, max_hidden=H, device=0)
     stream = torch.cuda.current_stream().cuda_stream
 
     def caller(t):
@@ -383,11 +399,10 @@ def main():
         ref, cpu = cpu_baseline(x, res, w, eps, args.cpu_budget)
         log("cpu oracle: %.2f GB/s (%s)" % (cpu["value"], cpu["sample"]))
         s0 = pool.sets(T)[0]
-        import numpy as np
         A.arrms_fused(op.handle, s0[0], W, T, H, s0[1], pool.weight.data_ptr(), eps, s0[2], s0[3], stream)
         torch.cuda.synchronize()
-        ro = synth.bits(pool.slot[0, W + 1].cpu())
-        no = synth.bits(pool.slot[0, W + 2].cpu())
+        ro = synth.bits(pool.slot[0, W + 1, :T].cpu())
+        no = synth.bits(pool.slot[0, W + 2, :T].cpu())
         parity = {"residual_out_mismatches": int((ro != ref["residual_out"]).sum()),
                   "norm_out_not_bit_identical": int((no != ref["norm_out"]).sum()),
                   "elements": int(ro.size)}
@@ -423,15 +438,40 @@ def main():
                                    100 * row["frac_peak_back_to_back"], row["us_event_pair_p50"],
                                    row["us_isolated_p50"], row["us_graph_replay"]))
 
+    # ---- per-call fixed time and streaming rate: least-squares line through the
+    # back-to-back GPU time at T = 4096, 8192, 16384 (same kernel, same layout)
+    fit = None
+    if not args.no_sweep:
+        pts = []
+        for t in FIT_T:
+            c = caller(t)
+            for _ in range(50):
+                c()
+            _, g = time_back_to_back(torch, c, 500)
+            pts.append((t, g * 1e3))
+        n = len(pts)
+        mt = sum(p[0] for p in pts) / n
+        mu = sum(p[1] for p in pts) / n
+        slope = sum((p[0] - mt) * (p[1] - mu) for p in pts) / sum((p[0] - mt) ** 2 for p in pts)
+        icpt = mu - slope * mt
+        row_bytes = 2 * H * (W + 3)
+        fit = {"points_us": [{"T": t, "us": u} for t, u in pts], "fixed_us_per_call": icpt,
+               "us_per_row": slope, "streaming_GB_s": row_bytes / (slope * 1e-6) / 1e9,
+               "streaming_frac_of_peak": row_bytes / (slope * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        log("fit over T=%s: fixed %.2f us per call, streaming %.0f GB/s (%.1f%% of peak)" % (
+            FIT_T, icpt, fit["streaming_GB_s"], 100 * fit["streaming_frac_of_peak"]))
+
     # ---- fusion: the page's two-stage form (rank sum kernel, then the epilogue as a
     # one-rank fused call through a BF16 `reduced` tensor) against the fused call
     fusion = None
     reduce_sweep = []
     if not args.no_sweep:
-        red_pool = torch.empty((POOL_SLOTS, T, H), dtype=torch.bfloat16, device="cuda")
+        red_pool = torch.empty((POOL_SLOTS, pool.T, H), dtype=torch.bfloat16, device="cuda")
         rcall = ReduceCaller(A, op.handle, pool, W, T, red_pool.data_ptr(), stream)
-        epi_sets = [([red_pool.data_ptr() + (i % POOL_SLOTS) * T * H * 2], st[1], st[2], st[3])
+        per_slot = len(pool.sets(T)) // POOL_SLOTS
+        epi_sets = [([pool.reduced_ptr(red_pool.data_ptr(), T, i // POOL_SLOTS, i % POOL_SLOTS)], st[1], st[2], st[3])
                     for i, st in enumerate(pool.sets(T))]
+        assert len(epi_sets) == per_slot * POOL_SLOTS
         ecall = Caller(A, op.handle, epi_sets, 1, T, H, pool.weight.data_ptr(), eps, stream)
 
         def two_stage():
@@ -500,6 +540,7 @@ def main():
         "parity_vs_oracle": parity,
         "sweep": sweep,
         "fusion": fusion,
+        "fixed_and_streaming": fit,
         "reduce_only": reduce_sweep,
         "copy_context": copy,
         "launch_floor_graph_us": floor_us,
