@@ -288,6 +288,28 @@ def copy_context(torch, nbytes):
     return {"bytes_per_copy": 2 * n * 2, "ms": ms, "GB_s": 2 * n * 2 / (ms * 1e-3) / 1e9}
 
 
+def copy_same_bytes(torch, nbytes, pairs=10, reps=200):
+    """A plain device-to-device copy moving the fused call's algorithmic bytes (nbytes/2 read,
+    nbytes/2 written), rotating over `pairs` source/destination pairs so that, like the
+    fused calls, successive copies touch fresh memory.  Context for the headline."""
+    n = nbytes // 4  # BF16 elements per copy: n*2 bytes read + n*2 written = nbytes
+    src = torch.empty((pairs, n), dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    for i in range(2 * pairs):
+        dst[i % pairs].copy_(src[i % pairs])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        dst[i % pairs].copy_(src[i % pairs])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return {"bytes_per_copy": 4 * n, "pairs": pairs, "us": ms * 1e3, "GB_s": 4 * n / (ms * 1e-3) / 1e9}
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -299,7 +321,8 @@ def cpu_model() -> str:
 
 
 def cpu_baseline(x, res, w, eps, budget_s):
-    """The oracle (single-threaded scalar C) on whole prefill calls, repeated up to budget_s."""
+    """The oracle (scalar C) on whole prefill calls: single-threaded for up to budget_s, then with
+    the rows split over the host threads for up to budget_s / 2."""
     import oracle
     import synth
     xb, rb, wb = synth.bits(x), synth.bits(res), synth.bits(w)
@@ -314,6 +337,24 @@ def cpu_baseline(x, res, w, eps, budget_s):
         if time.perf_counter() - t_start >= budget_s or len(times) >= 200:
             break
     med = statistics.median(times)
+    # the same oracle with the row range split over host threads (rows are independent)
+    try:
+        nthreads = min(16, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        nthreads = min(16, os.cpu_count() or 1)
+    ttimes = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.fused(xb, rb, wb, eps, threads=nthreads)
+        ttimes.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= budget_s / 2 or len(ttimes) >= 200:
+            break
+    tmed = statistics.median(ttimes)
+    threaded = {"value": algorithmic_bytes(W, T, H) / tmed / 1e9, "unit": "GB/s", "cores": nthreads,
+                "ms_per_call": tmed * 1e3, "repetitions": len(ttimes),
+                "sample": "the same whole call, rows split into %d contiguous ranges, one host thread each"
+                          % nthreads}
     return ref, {
         "value": algorithmic_bytes(W, T, H) / med / 1e9,
         "unit": "GB/s",
@@ -324,6 +365,7 @@ def cpu_baseline(x, res, w, eps, budget_s):
         "ms_per_call": med * 1e3,
         "cpu": cpu_model(),
         "host_threads_available": os.cpu_count(),
+        "threaded": threaded,
     }
 
 
@@ -397,7 +439,8 @@ def main():
     cpu = None
     if not args.no_cpu:
         ref, cpu = cpu_baseline(x, res, w, eps, args.cpu_budget)
-        log("cpu oracle: %.2f GB/s (%s)" % (cpu["value"], cpu["sample"]))
+        log("cpu oracle: %.2f GB/s (%s); %d threads: %.2f GB/s" % (
+            cpu["value"], cpu["sample"], cpu["threaded"]["cores"], cpu["threaded"]["value"]))
         s0 = pool.sets(T)[0]
         A.arrms_fused(op.handle, s0[0], W, T, H, s0[1], pool.weight.data_ptr(), eps, s0[2], s0[3], stream)
         torch.cuda.synchronize()
@@ -502,10 +545,34 @@ def main():
                 log("reduce only W=%d T=%5d: %.2f us, %.0f GB/s" % (w_, t, ms * 1e3, b / (ms * 1e-3) / 1e9))
         del red_pool
 
+    # ---- each variant forced on the same shapes (the automatic choice is one of them)
+    variants = []
+    if not args.no_sweep:
+        names = {A.ARRMS_VARIANT_ROW: "row", A.ARRMS_VARIANT_SPLITH: "splith", A.ARRMS_VARIANT_SCALAR: "scalar"}
+        for v, name in names.items():
+            op.set_variant(v)
+            for t in (1, 16, 128, 4096):
+                c = caller(t)
+                p = op.plan(pool.slot[0, :W, :t], pool.slot[0, W, :t], pool.weight, eps,
+                            pool.slot[0, W + 1, :t], pool.slot[0, W + 2, :t])
+                for _ in range(50):
+                    c()
+                _, g = time_back_to_back(torch, c, 1000 if t <= 128 else 300)
+                b = algorithmic_bytes(W, t, H)
+                variants.append({"variant": name, "T": t, "grid": p["grid"], "block": p["block"],
+                                 "kernels": p["kernels"], "us_back_to_back_gpu": g * 1e3,
+                                 "GB_s": b / (g * 1e-3) / 1e9})
+                log("variant %-6s T=%5d: %.2f us (%.0f GB/s), grid %d x %d, %d kernel(s)" % (
+                    name, t, g * 1e3, b / (g * 1e-3) / 1e9, p["grid"], p["block"], p["kernels"]))
+        op.set_variant(A.ARRMS_VARIANT_AUTO)
+
     floor_us = launch_floor_graph_us(torch)
     log("launch floor (one-element kernel, graph replay): %.2f us" % floor_us)
     copy = copy_context(torch, 512 * 2 ** 20)
     log("copy context: %.1f GB/s" % copy["GB_s"])
+    copy_same = copy_same_bytes(torch, nbytes)
+    log("copy of the headline's byte count (%d B, rotating): %.2f us, %.1f GB/s" % (
+        copy_same["bytes_per_copy"], copy_same["us"], copy_same["GB_s"]))
     tr = traffic_record()
     op.close()
 
@@ -543,6 +610,8 @@ def main():
         "fixed_and_streaming": fit,
         "reduce_only": reduce_sweep,
         "copy_context": copy,
+        "copy_same_bytes": copy_same,
+        "variants": variants,
         "launch_floor_graph_us": floor_us,
         "device": {"name": props.name, "compute_units": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", None), "memory_GiB": props.total_memory / 2 ** 30},

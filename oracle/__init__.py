@@ -73,13 +73,15 @@ class Oracle:
         """binary32 value of BF16 bit pattern ``b`` (exact)."""
         return float(self.lib.oracle_widen_bf16(ctypes.c_uint16(b)))
 
-    def fused(self, x, residual, weight, eps: float, rows: tuple[int, int] | None = None):
+    def fused(self, x, residual, weight, eps: float, rows: tuple[int, int] | None = None, threads: int = 1):
         """Run the operator on BF16 bit patterns.
 
         x        : uint16 [W, T, H] (or a sequence of W uint16 [T, H] arrays)
         residual : uint16 [T, H]
         weight   : uint16 [H]
         rows     : optional (begin, end) row range; other rows of the outputs stay 0
+        threads  : split the row range into this many contiguous pieces, one host thread
+                   each (rows are independent, so the result does not depend on it)
 
         Returns a dict of uint16 arrays ``reduced``, ``residual_out``, ``norm_out``
         ([T, H] each) and the binary32 per-row ``inv_rms`` [T].
@@ -97,14 +99,31 @@ class Oracle:
         b, e = rows if rows is not None else (0, T)
         ptrs = (ctypes.c_void_p * W)(*[p.ctypes.data for p in xs])
         out = {k: np.zeros((T, H), dtype=np.uint16) for k in ("reduced", "residual_out", "norm_out")}
-        inv = np.zeros(T, dtype=np.float32)
-        rc = self.lib.oracle_fused_rows(W, T, H, ptrs, residual.ctypes.data, weight.ctypes.data,
-                                        ctypes.c_float(eps), out["reduced"].ctypes.data,
-                                        out["residual_out"].ctypes.data, out["norm_out"].ctypes.data,
-                                        inv.ctypes.data, b, e)
-        if rc != 0:
+        out["inv_rms"] = np.zeros(T, dtype=np.float32)
+        ranges = [(b, e)]
+        if threads > 1 and e - b > 1:
+            n = min(threads, e - b)
+            ranges = [(b + (e - b) * i // n, b + (e - b) * (i + 1) // n) for i in range(n)]
+        status = [0] * len(ranges)
+
+        def run(i):
+            rb, re_ = ranges[i]
+            status[i] = self.lib.oracle_fused_rows(
+                W, T, H, ptrs, residual.ctypes.data, weight.ctypes.data, ctypes.c_float(eps),
+                out["reduced"].ctypes.data, out["residual_out"].ctypes.data, out["norm_out"].ctypes.data,
+                out["inv_rms"].ctypes.data, rb, re_)
+
+        if len(ranges) == 1:
+            run(0)
+        else:
+            # rows are independent; ctypes releases the GIL during each foreign call
+            workers = [threading.Thread(target=run, args=(i,)) for i in range(len(ranges))]
+            for t in workers:
+                t.start()
+            for t in workers:
+                t.join()
+        if any(status):
             raise ValueError("oracle rejected its arguments")
-        out["inv_rms"] = inv
         return out
 
 
@@ -132,5 +151,5 @@ def widen_bf16(b: int) -> float:
     return default().widen_bf16(b)
 
 
-def fused(x, residual, weight, eps: float, rows: tuple[int, int] | None = None):
-    return default().fused(x, residual, weight, eps, rows)
+def fused(x, residual, weight, eps: float, rows: tuple[int, int] | None = None, threads: int = 1):
+    return default().fused(x, residual, weight, eps, rows, threads)

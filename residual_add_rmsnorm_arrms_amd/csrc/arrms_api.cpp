@@ -200,9 +200,11 @@ int plan_splith(int cu_count, int max_hidden, int world, int tokens, int hidden,
     return ARRMS_OK;
 }
 
+// One row per workgroup, kScalarSpan (8) elements per lane per span: enough
+// whole waves to cover the row in one span, at most 1024 lanes.
 void plan_scalar(int tokens, int hidden, arrms_plan_t* p) {
-    int block = (hidden + 63) / 64 * 64;
-    if (block > 256) block = 256;
+    int block = ((hidden + 7) / 8 + 63) / 64 * 64;
+    if (block > 1024) block = 1024;
     p->variant = ARRMS_VARIANT_SCALAR;
     p->vec_per_thread = 0;
     p->threads_per_row = block;

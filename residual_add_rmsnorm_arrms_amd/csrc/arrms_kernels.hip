@@ -186,39 +186,94 @@ __global__ void __launch_bounds__(1024) splith_norm_kernel(const Args a) {
 }
 
 // -------------------------------------------------------------- scalar variant
-// Any H and any 2-byte alignment: one row per workgroup, one BF16 element per
-// lane per step.  residual_out is written in the first pass and re-read in the
-// second by the same lane (same addresses, program order), so H is unbounded.
-__global__ void __launch_bounds__(256) scalar_kernel(const Args a) {
+// Any H and any 2-byte alignment: one row per workgroup of n lanes (n <= 1024).
+// The row is walked in spans of kScalarSpan * n elements; in a span, lane l owns
+// elements l, l + n, ..., l + (kScalarSpan - 1) * n, so each 2-byte load
+// instruction of a wave covers 128 contiguous bytes.  Indexes past H are clamped
+// for loads (which stay inside the row, in one basic block, so the compiler can
+// issue the span's loads of every rank together) and masked for stores and for
+// the sum of squares.  When the row fits one span, residual_out stays in
+// registers for the second pass; otherwise the second pass re-reads it (each
+// element is read back by the lane that stored it, after the barrier).
+constexpr int kScalarSpan = 8;
+
+template <int W>
+__global__ void __launch_bounds__(1024) scalar_kernel(const Args a) {
+    const int world = W > 0 ? W : a.world;
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
-    const int nthreads = blockDim.x;
+    const int n = blockDim.x;
     const int H = a.hidden;
+    const int span = kScalarSpan * n;
     const size_t base = static_cast<size_t>(row) * static_cast<size_t>(H);
-    const uint16_t* res = static_cast<const uint16_t*>(a.residual);
+    const uint16_t* res = static_cast<const uint16_t*>(a.residual) + base;
     const uint16_t* w = static_cast<const uint16_t*>(a.weight);
-    uint16_t* ro_out = static_cast<uint16_t*>(a.residual_out);
-    uint16_t* n_out = static_cast<uint16_t*>(a.norm_out);
+    uint16_t* ro_out = static_cast<uint16_t*>(a.residual_out) + base;
+    uint16_t* n_out = static_cast<uint16_t*>(a.norm_out) + base;
 
     double ss = 0.0;
-    for (int h = tid; h < H; h += nthreads) {
-        float acc = lo_f32(static_cast<const uint16_t*>(a.x.p[0])[base + h]);
-        for (int r = 1; r < a.world; ++r) acc = acc + lo_f32(static_cast<const uint16_t*>(a.x.p[r])[base + h]);
-        const uint16_t o = cvt1(lo_f32(cvt1(acc)) + lo_f32(res[base + h]));
-        ro_out[base + h] = o;
-        const double d = static_cast<double>(lo_f32(o));
-        ss = __builtin_fma(d, d, ss);
+    uint16_t keep[kScalarSpan];  // residual_out of the last span
+    uint16_t wk[kScalarSpan];    // weight of the first span, loaded with the first span's inputs
+    for (int h0 = 0; h0 < H; h0 += span) {
+        float acc[kScalarSpan];
+        uint16_t rs[kScalarSpan];
+        const uint16_t* x0 = static_cast<const uint16_t*>(a.x.p[0]) + base;
+#pragma unroll
+        for (int u = 0; u < kScalarSpan; ++u) {
+            const int h = min(h0 + u * n + tid, H - 1);
+            acc[u] = lo_f32(x0[h]);
+            rs[u] = res[h];
+            if (h0 == 0) wk[u] = w[h];
+        }
+        // rank order 0, 1, ..., W-1 for every element
+#pragma unroll
+        for (int r = 1; r < (W > 0 ? W : kMaxWorld); ++r) {
+            if (W == 0 && r >= world) break;
+            const uint16_t* xr = static_cast<const uint16_t*>(a.x.p[r]) + base;
+#pragma unroll
+            for (int u = 0; u < kScalarSpan; ++u) acc[u] = acc[u] + lo_f32(xr[min(h0 + u * n + tid, H - 1)]);
+        }
+#pragma unroll
+        for (int u = 0; u < kScalarSpan; ++u) {
+            const int h = h0 + u * n + tid;
+            const uint16_t o = cvt1(lo_f32(cvt1(acc[u])) + lo_f32(rs[u]));
+            keep[u] = o;
+            if (h < H) {
+                ro_out[h] = o;
+                const double d = static_cast<double>(lo_f32(o));
+                ss = __builtin_fma(d, d, ss);
+            }
+        }
     }
-    __shared__ double wave_ss[4];
+    __shared__ double wave_ss[16];
     ss = seg_sum(ss, 64);
     if ((tid & 63) == 0) wave_ss[tid >> 6] = ss;
     __syncthreads();
     double total = wave_ss[0];
-    for (int i = 1; i < (nthreads >> 6); ++i) total = total + wave_ss[i];
+    for (int i = 1; i < (n >> 6); ++i) total = total + wave_ss[i];
     const float inv = inv_rms(total, a.hidden_d, a.eps);
-    for (int h = tid; h < H; h += nthreads) {
-        const float n = (lo_f32(ro_out[base + h]) * inv) * lo_f32(w[h]);
-        n_out[base + h] = cvt1(n);
+
+    if (H <= span) {
+#pragma unroll
+        for (int u = 0; u < kScalarSpan; ++u) {
+            const int h = u * n + tid;
+            if (h < H) n_out[h] = cvt1((lo_f32(keep[u]) * inv) * lo_f32(wk[u]));
+        }
+        return;
+    }
+    for (int h0 = 0; h0 < H; h0 += span) {
+        uint16_t rv[kScalarSpan], wv[kScalarSpan];
+#pragma unroll
+        for (int u = 0; u < kScalarSpan; ++u) {
+            const int h = min(h0 + u * n + tid, H - 1);
+            rv[u] = ro_out[h];
+            wv[u] = w[h];
+        }
+#pragma unroll
+        for (int u = 0; u < kScalarSpan; ++u) {
+            const int h = h0 + u * n + tid;
+            if (h < H) n_out[h] = cvt1((lo_f32(rv[u]) * inv) * lo_f32(wv[u]));
+        }
     }
 }
 
@@ -305,7 +360,19 @@ hipError_t launch_splith(const Args& a, int vpt, int grid, int block, hipStream_
 }
 
 hipError_t launch_scalar(const Args& a, int grid, int block, hipStream_t s) {
-    return launch(reinterpret_cast<const void*>(&scalar_kernel), a, grid, block, s);
+    const void* fn = nullptr;
+    switch (a.world) {
+        case 1: fn = reinterpret_cast<const void*>(&scalar_kernel<1>); break;
+        case 2: fn = reinterpret_cast<const void*>(&scalar_kernel<2>); break;
+        case 3: fn = reinterpret_cast<const void*>(&scalar_kernel<3>); break;
+        case 4: fn = reinterpret_cast<const void*>(&scalar_kernel<4>); break;
+        case 5: fn = reinterpret_cast<const void*>(&scalar_kernel<5>); break;
+        case 6: fn = reinterpret_cast<const void*>(&scalar_kernel<6>); break;
+        case 7: fn = reinterpret_cast<const void*>(&scalar_kernel<7>); break;
+        case 8: fn = reinterpret_cast<const void*>(&scalar_kernel<8>); break;
+        default: fn = reinterpret_cast<const void*>(&scalar_kernel<0>); break;
+    }
+    return launch(fn, a, grid, block, s);
 }
 
 }  // namespace arrms

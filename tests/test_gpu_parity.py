@@ -88,6 +88,20 @@ def test_world_sweep(W, variant):
     parity(W, 33, 2048, variant=variant, seed=100 + W)
 
 
+# The scalar variant walks a row in spans of 8 * lanes elements (lanes <= 1024): one
+# span keeps residual_out in registers, more spans re-read it; single-element rows,
+# rows ending one element into a new span, in place, generic W and the largest H.
+SCALAR_SPANS = [(4, 5, 1, False), (3, 7, 3, False), (4, 9, 8191, False), (4, 9, 8193, True),
+                (9, 6, 20001, True), (2, 3, 65535, False), (8, 3, 65536, True), (16, 2, 9000, False)]
+
+
+@pytest.mark.parametrize("W,T,H,inplace", SCALAR_SPANS)
+def test_scalar_spans(W, T, H, inplace):
+    plan, _ = parity(W, T, H, variant=SCALAR, inplace=inplace, seed=H)
+    assert plan["variant"] == SCALAR
+    assert plan["block"] == min(1024, -(-(-(-H // 8)) // 64) * 64)
+
+
 def _row_tunings(W, H):
     nvec = H // 8
     out = []
