@@ -32,6 +32,7 @@ import torch
 
 import synth
 from tests.bf16util import bf16_bits_exact, bf16_ulp, bf16_value, bf16_values
+from tests.exact_ieee import check_bit_exact
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_rows.txt")
 
@@ -319,6 +320,44 @@ def pin_inv_rms_is_correctly_rounded(orc):
             assert out["inv_rms"][t] == _nearest_f32(exact), (W, H, t)
 
 
+def pin_exact_emulation(orc, W, T, H, eps, sigma, outlier_p):
+    """Every output bit equals an exact rational emulation of the IEEE steps."""
+    wl = synth.Workload("exact", world=W, tokens=T, hidden=H, x_sigma=sigma, eps=eps, outlier_p=outlier_p,
+                        seed=70 + W)
+    x, res, w = synth.make_inputs(wl)
+    check_bit_exact(orc, synth.bits(x), synth.bits(res), synth.bits(w), eps)
+
+
+def _bf16_rne_f32(a: np.ndarray) -> np.ndarray:
+    """Input search helper: binary32 array rounded to BF16 (as binary32), nearest even."""
+    u = a.astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32)
+
+
+def pin_exact_emulation_order_sensitive_rows(orc):
+    """Rows where the order of the two final products matters after BF16 rounding.
+
+    (ro * inv) * w and (ro * w) * inv differ in one binary32 ulp now and then, which
+    BF16 rounding almost always hides; random workloads rarely expose the order.
+    Rows are searched (seeded, in numpy binary32) where the two orders give different
+    BF16 values, then the oracle is checked bit for bit against the exact emulation on
+    them (W=1 and a zero residual, so residual_out is the searched row itself)."""
+    rng = np.random.default_rng(123)
+    T, H, eps = 1 << 18, 16, 1e-6  # about 8 such elements expected per million
+    ro = _bf16_rne_f32(rng.standard_normal((T, H)).astype(np.float32))
+    w = _bf16_rne_f32(rng.uniform(0.5, 1.5, H).astype(np.float32))
+    ss = np.cumsum(ro.astype(np.float64) ** 2, axis=1)[:, -1]          # sequential in h
+    inv = (1.0 / np.sqrt(ss / H + float(np.float32(eps)))).astype(np.float32)[:, None]
+    a = _bf16_rne_f32((ro * inv).astype(np.float32) * w)
+    b = _bf16_rne_f32((ro * w).astype(np.float32) * inv)
+    rows = np.nonzero((a != b).any(axis=1))[0][:6]
+    assert len(rows) >= 3, "search found too few order-sensitive rows"
+    to_bits = lambda v: (np.ascontiguousarray(v, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    x = to_bits(ro[rows])[None]
+    check_bit_exact(orc, x, np.zeros((len(rows), H), dtype=np.uint16), to_bits(w), eps)
+
+
 PINS = [
     ("round_bf16_vs_torch", pin_round_bf16_matches_torch_conversion, {}),
     ("round_bf16_nan_overflow", pin_round_bf16_nan_and_overflow, {}),
@@ -338,4 +377,9 @@ PINS = [
     ("rank_permutation_exact", pin_rank_permutation_exact_sums, {}),
     ("row_range_determinism", pin_row_range_and_determinism, {}),
     ("rows_independent", pin_rows_are_independent, {}),
+    *[("exact_emulation_W%d_H%d" % (W, H), pin_exact_emulation,
+       {"W": W, "T": T, "H": H, "eps": eps, "sigma": sg, "outlier_p": op})
+      for W, T, H, eps, sg, op in [(2, 4, 128, 1e-6, 1.0, 0.0), (5, 2, 72, 1e-6, 1.0, 0.05),
+                                   (3, 2, 40, 0.5, 0.25, 0.0)]],
+    ("exact_emulation_order_sensitive", pin_exact_emulation_order_sensitive_rows, {}),
 ]

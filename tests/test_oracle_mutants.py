@@ -39,6 +39,12 @@ MUTANTS = [
     ("truncate_not_round", "kept += 1u;", "kept += 0u;"),
     ("nan_not_quieted", "return (uint16_t)((u >> 16) | 0x0040u);", "return (uint16_t)(u >> 16);"),
     ("widen_wrong_shift", "uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+    ("scale_before_normalise",
+     "const float normed = widen(residual_out[row + h]) * inv;\n            const float scaled = normed * widen(weight[h]);",
+     "const float normed = widen(residual_out[row + h]) * widen(weight[h]);\n            const float scaled = normed * inv;"),
+    ("inv_rounded_before_reciprocal", "(float)(1.0 / sqrt(mean_sq + (double)eps))",
+     "1.0f / (float)sqrt(mean_sq + (double)eps)"),
+    ("rank_sum_in_binary64", "float acc = widen(x[0][row + h]);", "double acc = widen(x[0][row + h]);"),
 ]
 
 
