@@ -418,7 +418,8 @@ def main():
 
     # ---- headline: T=4096, K timed steps between synchronisations
     call = caller(T)
-    plan = op.plan(pool.slot[0, :W], pool.slot[0, W], pool.weight, eps, pool.slot[0, W + 1], pool.slot[0, W + 2])
+    plan = op.plan(pool.slot[0, :W, :T], pool.slot[0, W, :T], pool.weight, eps, pool.slot[0, W + 1, :T],
+                   pool.slot[0, W + 2, :T])
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
