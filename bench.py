@@ -15,6 +15,9 @@ pool of distinct input/output sets (10 slots of 16384 rows; far more than the
 T = 4096, 8192, 16384 (beyond the metric's range) separate the per-call fixed time
 from the kernel's streaming rate.
 
+`--workload large_hidden` (W=8 T=8192 H=8192) or `--workload ragged_outliers`
+(W=8 T=16383 H=5120, 1% outliers) times those shapes instead, headline only.
+
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -42,7 +45,12 @@ POOL_SLOTS = 10
 # the fused kernels and the device helpers they include
 KERNEL_SRC = [os.path.join(ROOT, "residual_add_rmsnorm_arrms_amd", "csrc", f)
               for f in ("arrms_device.h", "arrms_kernels.hip")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_w4_h2048_t4096.json")
+# workloads the benchmark can time (--workload); the default is the metric's own
+BENCH_WORKLOADS = ("prefill", "large_hidden", "ragged_outliers")
+
+
+def traffic_file(wl) -> str:
+    return os.path.join(ROOT, "profiles", "traffic_%s_w%d_h%d_t%d.json" % (wl.name, wl.world, wl.hidden, wl.tokens))
 
 
 def log(*a):
@@ -369,12 +377,13 @@ def cpu_baseline(x, res, w, eps, budget_s):
     }
 
 
-def traffic_record():
-    """FETCH_SIZE / WRITE_SIZE per launch measured by rocprofv3 for the current kernel source,
-    or None when the counters were taken on another version of the kernels."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_record(wl):
+    """FETCH_SIZE / WRITE_SIZE per launch measured by rocprofv3 for the current kernel source
+    on workload wl, or None when the counters were taken on another version of the kernels."""
+    path = traffic_file(wl)
+    if not os.path.exists(path):
         return None
-    rec = json.load(open(TRAFFIC_FILE))
+    rec = json.load(open(path))
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return rec
@@ -388,7 +397,12 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-sweep", action="store_true", help="only the T=4096 headline")
+    ap.add_argument("--workload", default="prefill", choices=BENCH_WORKLOADS,
+                    help="headline workload (the T sweep, fit, fusion, variant and rank-sum sections run "
+                         "only for prefill, the metric's W=4 H=2048 shape)")
     args = ap.parse_args()
+    if args.workload != "prefill":
+        args.no_sweep = True
 
     if args.gpus != 1:
         print("bench.py measures one GPU: the partial sums of all ranks are modelled as buffers already "
@@ -404,13 +418,16 @@ def main():
         __graft_entry__.build()
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
-    wl = synth.WORKLOADS["prefill"]
+    wl = synth.WORKLOADS[args.workload]
     W, T, H, eps = wl.world, wl.tokens, wl.hidden, wl.eps
     log("generating inputs W=%d T=%d H=%d" % (W, T, H))
     x, res, w = synth.make_inputs(wl)
-    pool = Pool(torch, x, res, w, rows=POOL_ROWS)
+    # prefill: 16384-row slots, so the T <= 16384 points of the fit also rotate; larger
+    # workloads: one call per slot (each slot alone is far beyond the Infinity Cache)
+    pool_rows = POOL_ROWS if 4 * T <= POOL_ROWS else T
+    pool = Pool(torch, x, res, w, rows=pool_rows)
     log("pool: %d slots, %.2f GiB" % (POOL_SLOTS, pool.nbytes / 2 ** 30))
-    op = A.FusedReduceResidualRMSNorm(max_world=8, max_tokens=POOL_ROWS, max_hidden=H, device=0)
+    op = A.FusedReduceResidualRMSNorm(max_world=max(8, W), max_tokens=pool_rows, max_hidden=H, device=0)
     stream = torch.cuda.current_stream().cuda_stream
 
     def caller(t):
@@ -571,15 +588,16 @@ def main():
     log("launch floor (one-element kernel, graph replay): %.2f us" % floor_us)
     copy = copy_context(torch, 512 * 2 ** 20)
     log("copy context: %.1f GB/s" % copy["GB_s"])
-    copy_same = copy_same_bytes(torch, nbytes)
+    copy_same = copy_same_bytes(torch, nbytes, pairs=max(2, min(10, int(4e9 // nbytes))))
     log("copy of the headline's byte count (%d B, rotating): %.2f us, %.1f GB/s" % (
         copy_same["bytes_per_copy"], copy_same["us"], copy_same["GB_s"]))
-    tr = traffic_record()
+    tr = traffic_record(wl)
     op.close()
 
     value = nbytes / (wall_ms * 1e-3) / 1e9
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "prefill" else
+        "achieved HBM GB/s (%% of peak) and µs/call, W=%d H=%d T=%d" % (W, H, T),
         "value": value,
         "unit": "GB/s",
         "n_gpus": 1,
@@ -590,8 +608,11 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded SplitMix64/Box-Muller; x~N(0,0.5^2), residual~N(0,1), weight~U(0.5,1.5))",
-        "config": {"workload": "prefill: W=4 rank partials, T=4096 tokens, H=2048, BF16 in/out, eps=1e-6",
+        "data": "synthetic (seeded SplitMix64/Box-Muller; x~N(0,%g^2)%s, residual~N(0,%g^2), weight~U(%g,%g))" % (
+            wl.x_sigma, (", %g%% of x elements scaled x%g" % (100 * wl.outlier_p, wl.outlier_scale))
+            if wl.outlier_p else "", wl.residual_sigma, wl.weight_lo, wl.weight_hi),
+        "config": {"workload": "%s: W=%d rank partials, T=%d tokens, H=%d, BF16 in/out, eps=%g" % (
+                   wl.name, W, T, H, eps),
                    "world": W, "tokens": T, "hidden": H, "io_dtype": "bf16", "accumulate": "f32 rank sum, f64 "
                    "sum of squares", "algorithmic_bytes_per_call": nbytes, "plan": plan,
                    "pool_bytes": pool.nbytes, "parallelism": "1 GPU"},
