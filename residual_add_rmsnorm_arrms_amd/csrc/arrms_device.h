@@ -55,16 +55,16 @@ __device__ __forceinline__ void st4_stream(void* base, size_t i, u32x4 v) {
 // the i-th workgroup an XCD receives takes logical block (8 * (i / K) + x) * K
 // + i % K (x = its XCD): runs of K consecutive blocks (rows) stay on one XCD,
 // and at any moment the 8 XCDs work on neighbouring runs.  K = 0 keeps the
-// hardware's round-robin order.  Returns -1 for padding blocks past a.blocks.
-__device__ __forceinline__ int logical_block(const Args& a) {
+// hardware's round-robin order.  Returns -1 for padding blocks past `blocks`.
+__device__ __forceinline__ int logical_block(int xcd_chunk, int blocks) {
     const int b = blockIdx.x;
-    const int k = a.xcd_chunk;
+    const int k = xcd_chunk;
     if (k == 0) return b;
     const int x = b & 7;
     const int i = b >> 3;
     const int j = i / k;
     const int l = (j * 8 + x) * k + (i - j * k);
-    return l < a.blocks ? l : -1;
+    return l < blocks ? l : -1;
 }
 
 // ---------------------------------------------------------------- reductions

@@ -16,7 +16,8 @@ struct Partials {
     const void* p[kMaxWorld];
 };
 
-// Kernel arguments, shared by every variant (passed by value).
+// One call's description, filled by the host code; each launcher packs the
+// fields its kernel needs into that kernel's argument block (below).
 struct Args {
     Partials x;             // W device pointers, BF16 [tokens][hidden]
     const void* residual;   // BF16 [tokens][hidden]
@@ -39,6 +40,106 @@ struct Args {
     int xcd_chunk;          // K > 0: runs of K consecutive blocks per XCD (grid a multiple of 8K)
     long long count;        // rank sum only: elements (tokens * hidden)
 };
+
+// ------------------------------------------------- per-kernel argument blocks
+// What each kernel receives, packed from Args by its launcher.  On MI355X with
+// ROCm 7 the host cost of a launch steps from about 2.8 us to about 3.7 us when
+// the explicit kernel arguments grow past 112 bytes, and reading blockDim or
+// gridDim in a kernel adds the implicit-argument block (about 0.3 us more).  So
+// the blocks below stay within 112 bytes for every W <= 8 (the generic and
+// W = 16 kernels carry 16 pointers and are larger), and the kernels take their
+// sizes from these fields, never from blockDim or gridDim.  Small sizes share
+// one packed word.
+
+// The partial pointers: W of them for kernels specialised on W, 16 otherwise.
+template <int WA>
+struct Ptrs {
+    const void* p[WA];
+};
+
+// Row variant.  shape: bits 0-15 nvec (H / 8), 16-22 threads_per_row / 16,
+// 23-25 log2(rows_per_block), 26-30 W.
+template <int WA>
+struct RowArgs {
+    Ptrs<WA> x;
+    const void* residual;
+    const void* weight;
+    void* residual_out;
+    void* norm_out;
+    float eps;
+    int tokens;
+    int xcd_chunk;
+    uint32_t shape;
+};
+
+// Split-H phase 1.  vec: bits 0-15 nvec, 16-31 chunk_vec; shape: bits 0-15
+// chunks per row, 16-20 W.  The workgroup has chunk_vec / VPT lanes.
+template <int WA>
+struct SplitPartialArgs {
+    Ptrs<WA> x;
+    const void* residual;
+    void* residual_out;
+    double* ws;
+    int blocks;
+    int xcd_chunk;
+    uint32_t vec;
+    uint32_t shape;
+};
+
+// Split-H phase 2.  vec as in phase 1; shape: bits 0-15 chunks per row,
+// 16-31 lanes per workgroup.
+struct SplitNormArgs {
+    const void* residual_out;
+    const void* weight;
+    void* norm_out;
+    const double* ws;
+    float eps;
+    int blocks;
+    int xcd_chunk;
+    uint32_t vec;
+    uint32_t shape;
+};
+
+// Element-wise variant.  shape: bits 0-15 lanes per workgroup, 16-20 W.
+template <int WA>
+struct ScalarArgs {
+    Ptrs<WA> x;
+    const void* residual;
+    const void* weight;
+    void* residual_out;
+    void* norm_out;
+    float eps;
+    int hidden;
+    uint32_t shape;
+};
+
+// Rank sum alone (256 lanes per workgroup).  grid: launched workgroups (the
+// element-wise kernel's grid stride).
+template <int WA>
+struct ReduceArgs {
+    Ptrs<WA> x;
+    void* reduced;
+    long long count;
+    int blocks;
+    int xcd_chunk;
+    int world;
+    int grid;
+};
+
+// The first WA partial pointers of a call (the rest of Ptrs<16> stays null).
+template <int WA>
+inline Ptrs<WA> pack_ptrs(const Args& a) {
+    Ptrs<WA> x = {};
+    for (int r = 0; r < a.world && r < WA; ++r) x.p[r] = a.x.p[r];
+    return x;
+}
+
+// Launch `fn` with one argument block passed by value.
+template <typename K>
+inline hipError_t launch_with(const void* fn, const K& args, int grid, int block, hipStream_t s) {
+    void* p[] = {const_cast<K*>(&args)};
+    return hipLaunchKernel(fn, dim3(grid), dim3(block), p, 0, s);
+}
 
 // Each launcher returns the hipError_t of the launch itself.
 hipError_t launch_row(const Args& a, int vec_per_thread, int grid, int block, hipStream_t s);

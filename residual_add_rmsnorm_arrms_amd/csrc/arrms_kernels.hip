@@ -46,18 +46,21 @@ constexpr int row_max_threads() {
 }
 
 template <int W, int VPT>
-__global__ void __launch_bounds__((row_max_threads<W, VPT>())) row_kernel(const Args a) {
+__global__ void __launch_bounds__((row_max_threads<W, VPT>())) row_kernel(const RowArgs<(W > 0 ? W : kMaxWorld)> a) {
     constexpr int WA = W > 0 ? W : kMaxWorld;
-    const int world = W > 0 ? W : a.world;
-    const int tpr = a.threads_per_row;
-    const int block = logical_block(a);
+    const int world = W > 0 ? W : static_cast<int>((a.shape >> 26) & 31u);
+    const int nvec = static_cast<int>(a.shape & 0xffffu);
+    const int tpr = static_cast<int>((a.shape >> 16) & 127u) * 16;
+    const int rpb_log2 = static_cast<int>((a.shape >> 23) & 7u);
+    const int blocks = (a.tokens + (1 << rpb_log2) - 1) >> rpb_log2;
+    const int block = logical_block(a.xcd_chunk, blocks);
     if (block < 0) return;  // padding workgroup of the XCD mapping (whole workgroup)
     const int tid = threadIdx.x;
     const int row_in_block = tid / tpr;
     const int lane = tid - row_in_block * tpr;
-    const int row = block * a.rows_per_block + row_in_block;
+    const int row = (block << rpb_log2) + row_in_block;
     const bool row_ok = row < a.tokens;
-    const size_t base = static_cast<size_t>(row_ok ? row : 0) * static_cast<size_t>(a.nvec);
+    const size_t base = static_cast<size_t>(row_ok ? row : 0) * static_cast<size_t>(nvec);
 
     bool ok[VPT];
     u32x4 xv[VPT][WA];
@@ -66,7 +69,7 @@ __global__ void __launch_bounds__((row_max_threads<W, VPT>())) row_kernel(const 
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         const int v = lane + k * tpr;
-        ok[k] = row_ok && v < a.nvec;
+        ok[k] = row_ok && v < nvec;
         if (ok[k]) {
 #pragma unroll
             for (int r = 0; r < WA; ++r)
@@ -98,7 +101,7 @@ __global__ void __launch_bounds__((row_max_threads<W, VPT>())) row_kernel(const 
         for (int i = 1; i < waves; ++i) t = t + wave_ss[first + i];
         ss = t;
     }
-    const float inv = inv_rms(ss, a.hidden_d, a.eps);
+    const float inv = inv_rms(ss, static_cast<double>(nvec * 8), a.eps);
 
 #pragma unroll
     for (int k = 0; k < VPT; ++k)
@@ -121,18 +124,22 @@ template <int W>
 constexpr int splith_max_threads() { return (W == 0 || W > 8) ? 512 : 1024; }
 
 template <int W, int VPT>
-__global__ void __launch_bounds__(splith_max_threads<W>()) splith_partial_kernel(const Args a) {
+__global__ void __launch_bounds__(splith_max_threads<W>())
+    splith_partial_kernel(const SplitPartialArgs<(W > 0 ? W : kMaxWorld)> a) {
     constexpr int WA = W > 0 ? W : kMaxWorld;
-    const int world = W > 0 ? W : a.world;
-    const int block = logical_block(a);
+    const int world = W > 0 ? W : static_cast<int>((a.shape >> 16) & 31u);
+    const int chunks = static_cast<int>(a.shape & 0xffffu);
+    const int nvec = static_cast<int>(a.vec & 0xffffu);
+    const int chunk_vec = static_cast<int>(a.vec >> 16);
+    const int block = logical_block(a.xcd_chunk, a.blocks);
     if (block < 0) return;
-    const int row = block / a.chunks;
-    const int chunk = block - row * a.chunks;
+    const int row = block / chunks;
+    const int chunk = block - row * chunks;
     const int tid = threadIdx.x;
-    const int nthreads = blockDim.x;
-    const int v0 = chunk * a.chunk_vec;
-    const int v1 = min(a.nvec, v0 + a.chunk_vec);
-    const size_t base = static_cast<size_t>(row) * static_cast<size_t>(a.nvec);
+    const int nthreads = chunk_vec / VPT;  // the workgroup size
+    const int v0 = chunk * chunk_vec;
+    const int v1 = min(nvec, v0 + chunk_vec);
+    const size_t base = static_cast<size_t>(row) * static_cast<size_t>(nvec);
 
     bool ok[VPT];
     u32x4 xv[VPT][WA];
@@ -164,24 +171,28 @@ __global__ void __launch_bounds__(splith_max_threads<W>()) splith_partial_kernel
     if (tid == 0) {
         double t = wave_ss[0];
         for (int i = 1; i < (nthreads >> 6); ++i) t = t + wave_ss[i];
-        a.ws[static_cast<size_t>(row) * a.chunks + chunk] = t;
+        a.ws[static_cast<size_t>(row) * chunks + chunk] = t;
     }
 }
 
-__global__ void __launch_bounds__(1024) splith_norm_kernel(const Args a) {
-    const int block = logical_block(a);
+__global__ void __launch_bounds__(1024) splith_norm_kernel(const SplitNormArgs a) {
+    const int chunks = static_cast<int>(a.shape & 0xffffu);
+    const int nthreads = static_cast<int>(a.shape >> 16);
+    const int nvec = static_cast<int>(a.vec & 0xffffu);
+    const int chunk_vec = static_cast<int>(a.vec >> 16);
+    const int block = logical_block(a.xcd_chunk, a.blocks);
     if (block < 0) return;
-    const int row = block / a.chunks;
-    const int chunk = block - row * a.chunks;
+    const int row = block / chunks;
+    const int chunk = block - row * chunks;
     const int tid = threadIdx.x;
-    const int v0 = chunk * a.chunk_vec;
-    const int v1 = min(a.nvec, v0 + a.chunk_vec);
-    const size_t base = static_cast<size_t>(row) * static_cast<size_t>(a.nvec);
-    const double* part = a.ws + static_cast<size_t>(row) * a.chunks;
+    const int v0 = chunk * chunk_vec;
+    const int v1 = min(nvec, v0 + chunk_vec);
+    const size_t base = static_cast<size_t>(row) * static_cast<size_t>(nvec);
+    const double* part = a.ws + static_cast<size_t>(row) * chunks;
     double total = part[0];
-    for (int c = 1; c < a.chunks; ++c) total = total + part[c];
-    const float inv = inv_rms(total, a.hidden_d, a.eps);
-    for (int v = v0 + tid; v < v1; v += blockDim.x)
+    for (int c = 1; c < chunks; ++c) total = total + part[c];
+    const float inv = inv_rms(total, static_cast<double>(nvec * 8), a.eps);
+    for (int v = v0 + tid; v < v1; v += nthreads)
         st4_stream(a.norm_out, base + v, norm_vec(ld4(a.residual_out, base + v), inv, ld4(a.weight, v)));
 }
 
@@ -198,11 +209,11 @@ __global__ void __launch_bounds__(1024) splith_norm_kernel(const Args a) {
 constexpr int kScalarSpan = 8;
 
 template <int W>
-__global__ void __launch_bounds__(1024) scalar_kernel(const Args a) {
-    const int world = W > 0 ? W : a.world;
+__global__ void __launch_bounds__(1024) scalar_kernel(const ScalarArgs<(W > 0 ? W : kMaxWorld)> a) {
+    const int world = W > 0 ? W : static_cast<int>((a.shape >> 16) & 31u);
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
-    const int n = blockDim.x;
+    const int n = static_cast<int>(a.shape & 0xffffu);  // the workgroup size
     const int H = a.hidden;
     const int span = kScalarSpan * n;
     const size_t base = static_cast<size_t>(row) * static_cast<size_t>(H);
@@ -251,7 +262,7 @@ __global__ void __launch_bounds__(1024) scalar_kernel(const Args a) {
     __syncthreads();
     double total = wave_ss[0];
     for (int i = 1; i < (n >> 6); ++i) total = total + wave_ss[i];
-    const float inv = inv_rms(total, a.hidden_d, a.eps);
+    const float inv = inv_rms(total, static_cast<double>(H), a.eps);
 
     if (H <= span) {
 #pragma unroll
@@ -278,9 +289,68 @@ __global__ void __launch_bounds__(1024) scalar_kernel(const Args a) {
 }
 
 // ---------------------------------------------------------------- launchers
-hipError_t launch(const void* fn, const Args& a, int grid, int block, hipStream_t s) {
-    void* args[] = {const_cast<Args*>(&a)};
-    return hipLaunchKernel(fn, dim3(grid), dim3(block), args, 0, s);
+// Argument blocks.  Each returns false when a size does not fit its packed
+// field (the planner never produces such a plan; the launch is then refused).
+template <int WA>
+bool row_args(const Args& a, RowArgs<WA>* r) {
+    const int tpr16 = a.threads_per_row / 16;
+    int rpb_log2 = 0;
+    while ((1 << rpb_log2) < a.rows_per_block) ++rpb_log2;
+    if (a.nvec > 0xffff || a.threads_per_row % 16 || tpr16 < 1 || tpr16 > 127 || (1 << rpb_log2) != a.rows_per_block ||
+        rpb_log2 > 7 || a.world > 31)
+        return false;
+    *r = RowArgs<WA>{};
+    r->x = pack_ptrs<WA>(a);
+    r->residual = a.residual;
+    r->weight = a.weight;
+    r->residual_out = a.residual_out;
+    r->norm_out = a.norm_out;
+    r->eps = a.eps;
+    r->tokens = a.tokens;
+    r->xcd_chunk = a.xcd_chunk;
+    r->shape = static_cast<uint32_t>(a.nvec) | static_cast<uint32_t>(tpr16) << 16 |
+               static_cast<uint32_t>(rpb_log2) << 23 | static_cast<uint32_t>(a.world) << 26;
+    return true;
+}
+
+template <int WA>
+hipError_t launch_row_with(const void* fn, const Args& a, int grid, int block, hipStream_t s) {
+    RowArgs<WA> r;
+    if (!row_args<WA>(a, &r)) return hipErrorInvalidValue;
+    return launch_with(fn, r, grid, block, s);
+}
+
+bool splith_fits(const Args& a, int block) {
+    return a.nvec <= 0xffff && a.chunk_vec <= 0xffff && a.chunks <= 0xffff && block <= 0xffff && a.world <= 31;
+}
+
+template <int WA>
+hipError_t launch_splith_partial_with(const void* fn, const Args& a, int grid, int block, hipStream_t s) {
+    SplitPartialArgs<WA> r{};
+    r.x = pack_ptrs<WA>(a);
+    r.residual = a.residual;
+    r.residual_out = a.residual_out;
+    r.ws = a.ws;
+    r.blocks = a.blocks;
+    r.xcd_chunk = a.xcd_chunk;
+    r.vec = static_cast<uint32_t>(a.nvec) | static_cast<uint32_t>(a.chunk_vec) << 16;
+    r.shape = static_cast<uint32_t>(a.chunks) | static_cast<uint32_t>(a.world) << 16;
+    return launch_with(fn, r, grid, block, s);
+}
+
+template <int WA>
+hipError_t launch_scalar_with(const void* fn, const Args& a, int grid, int block, hipStream_t s) {
+    if (block > 0xffff || a.world > 31) return hipErrorInvalidValue;
+    ScalarArgs<WA> r{};
+    r.x = pack_ptrs<WA>(a);
+    r.residual = a.residual;
+    r.weight = a.weight;
+    r.residual_out = a.residual_out;
+    r.norm_out = a.norm_out;
+    r.eps = a.eps;
+    r.hidden = a.hidden;
+    r.shape = static_cast<uint32_t>(block) | static_cast<uint32_t>(a.world) << 16;
+    return launch_with(fn, r, grid, block, s);
 }
 
 // Instantiated (W, VPT) pairs: those whose (W + 2) * VPT live vectors fit the
@@ -343,7 +413,18 @@ hipError_t launch_row(const Args& a, int vpt, int grid, int block, hipStream_t s
         default: return hipErrorInvalidValue;
     }
     if (!fn) return hipErrorInvalidValue;
-    return launch(fn, a, grid, block, s);
+    // row_kernel<W, VPT> takes RowArgs<W> for W <= 8 and RowArgs<16> otherwise
+    switch (a.world) {
+        case 1: return launch_row_with<1>(fn, a, grid, block, s);
+        case 2: return launch_row_with<2>(fn, a, grid, block, s);
+        case 3: return launch_row_with<3>(fn, a, grid, block, s);
+        case 4: return launch_row_with<4>(fn, a, grid, block, s);
+        case 5: return launch_row_with<5>(fn, a, grid, block, s);
+        case 6: return launch_row_with<6>(fn, a, grid, block, s);
+        case 7: return launch_row_with<7>(fn, a, grid, block, s);
+        case 8: return launch_row_with<8>(fn, a, grid, block, s);
+        default: return launch_row_with<kMaxWorld>(fn, a, grid, block, s);
+    }
 }
 
 hipError_t launch_splith(const Args& a, int vpt, int grid, int block, hipStream_t s) {
@@ -353,26 +434,46 @@ hipError_t launch_splith(const Args& a, int vpt, int grid, int block, hipStream_
         case 2: fn = splith_fn<2>(a.world); break;
         default: return hipErrorInvalidValue;
     }
-    if (!fn) return hipErrorInvalidValue;
-    const hipError_t e = launch(fn, a, grid, block, s);
+    if (!fn || !splith_fits(a, block) || a.chunk_vec != block * vpt) return hipErrorInvalidValue;
+    hipError_t e;
+    switch (a.world) {
+        case 1: e = launch_splith_partial_with<1>(fn, a, grid, block, s); break;
+        case 2: e = launch_splith_partial_with<2>(fn, a, grid, block, s); break;
+        case 3: e = launch_splith_partial_with<3>(fn, a, grid, block, s); break;
+        case 4: e = launch_splith_partial_with<4>(fn, a, grid, block, s); break;
+        case 5: e = launch_splith_partial_with<5>(fn, a, grid, block, s); break;
+        case 6: e = launch_splith_partial_with<6>(fn, a, grid, block, s); break;
+        case 7: e = launch_splith_partial_with<7>(fn, a, grid, block, s); break;
+        case 8: e = launch_splith_partial_with<8>(fn, a, grid, block, s); break;
+        default: e = launch_splith_partial_with<kMaxWorld>(fn, a, grid, block, s); break;
+    }
     if (e != hipSuccess) return e;
-    return launch(reinterpret_cast<const void*>(&splith_norm_kernel), a, grid, block, s);
+    SplitNormArgs n{};
+    n.residual_out = a.residual_out;
+    n.weight = a.weight;
+    n.norm_out = a.norm_out;
+    n.ws = a.ws;
+    n.eps = a.eps;
+    n.blocks = a.blocks;
+    n.xcd_chunk = a.xcd_chunk;
+    n.vec = static_cast<uint32_t>(a.nvec) | static_cast<uint32_t>(a.chunk_vec) << 16;
+    n.shape = static_cast<uint32_t>(a.chunks) | static_cast<uint32_t>(block) << 16;
+    return launch_with(reinterpret_cast<const void*>(&splith_norm_kernel), n, grid, block, s);
 }
 
 hipError_t launch_scalar(const Args& a, int grid, int block, hipStream_t s) {
-    const void* fn = nullptr;
     switch (a.world) {
-        case 1: fn = reinterpret_cast<const void*>(&scalar_kernel<1>); break;
-        case 2: fn = reinterpret_cast<const void*>(&scalar_kernel<2>); break;
-        case 3: fn = reinterpret_cast<const void*>(&scalar_kernel<3>); break;
-        case 4: fn = reinterpret_cast<const void*>(&scalar_kernel<4>); break;
-        case 5: fn = reinterpret_cast<const void*>(&scalar_kernel<5>); break;
-        case 6: fn = reinterpret_cast<const void*>(&scalar_kernel<6>); break;
-        case 7: fn = reinterpret_cast<const void*>(&scalar_kernel<7>); break;
-        case 8: fn = reinterpret_cast<const void*>(&scalar_kernel<8>); break;
-        default: fn = reinterpret_cast<const void*>(&scalar_kernel<0>); break;
+        case 1: return launch_scalar_with<1>(reinterpret_cast<const void*>(&scalar_kernel<1>), a, grid, block, s);
+        case 2: return launch_scalar_with<2>(reinterpret_cast<const void*>(&scalar_kernel<2>), a, grid, block, s);
+        case 3: return launch_scalar_with<3>(reinterpret_cast<const void*>(&scalar_kernel<3>), a, grid, block, s);
+        case 4: return launch_scalar_with<4>(reinterpret_cast<const void*>(&scalar_kernel<4>), a, grid, block, s);
+        case 5: return launch_scalar_with<5>(reinterpret_cast<const void*>(&scalar_kernel<5>), a, grid, block, s);
+        case 6: return launch_scalar_with<6>(reinterpret_cast<const void*>(&scalar_kernel<6>), a, grid, block, s);
+        case 7: return launch_scalar_with<7>(reinterpret_cast<const void*>(&scalar_kernel<7>), a, grid, block, s);
+        case 8: return launch_scalar_with<8>(reinterpret_cast<const void*>(&scalar_kernel<8>), a, grid, block, s);
+        default:
+            return launch_scalar_with<kMaxWorld>(reinterpret_cast<const void*>(&scalar_kernel<0>), a, grid, block, s);
     }
-    return launch(fn, a, grid, block, s);
 }
 
 }  // namespace arrms
