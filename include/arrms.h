@@ -124,7 +124,8 @@ int arrms_create(arrms_handle_t* out, int device, int max_world, int max_tokens,
  * anything else uses the scalar kernel with the same results.
  * All checks happen before anything is enqueued: an error has no side effect.
  * Returns ARRMS_OK, ARRMS_ERR_INVALID_ARG, ARRMS_ERR_UNSUPPORTED (a forced
- * variant cannot run this shape) or ARRMS_ERR_HIP (launch failure).
+ * variant cannot run this shape, or the launch would exceed 2^32 - 1 work-items,
+ * e.g. T * H beyond about 2^35 elements) or ARRMS_ERR_HIP (launch failure).
  */
 int arrms_fused(arrms_handle_t h, const void* const* partials, int world, int tokens, int hidden,
                 const void* residual, const void* weight, float eps, void* residual_out,

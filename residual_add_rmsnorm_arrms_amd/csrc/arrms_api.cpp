@@ -139,7 +139,7 @@ int plan_row(int world, int tokens, int hidden, const arrms_tuning_t* t, arrms_p
     p->rows_per_block = rpb;
     p->chunks_per_row = 1;
     p->block = best_tpr * rpb;
-    p->blocks = (tokens + rpb - 1) / rpb;
+    p->blocks = static_cast<int>((static_cast<long>(tokens) + rpb - 1) / rpb);
     p->kernels = 1;
     // Automatic XCD runs: about 3 MiB of traffic per run, a power of two of
     // blocks (measured best: 64 blocks at W=4 H=2048, 16 at W=8 H=5120/8192);
@@ -243,7 +243,21 @@ const char* arrms_status_string(int status) {
     }
 }
 
-int arrms_plan(int cu_count, int variant, const arrms_tuning_t* tuning, int max_world, int max_tokens,
+}  // extern "C"
+
+namespace {
+
+// A launch's grid in work-items (workgroups x lanes) is a 32-bit quantity on this
+// GPU; larger requests are refused at planning time rather than by the runtime.
+int check_grid(int rc, arrms_plan_t* plan) {
+    if (rc == ARRMS_OK && static_cast<long long>(plan->grid) * plan->block > 0xffffffffLL) {
+        memset(plan, 0, sizeof *plan);
+        return ARRMS_ERR_UNSUPPORTED;
+    }
+    return rc;
+}
+
+int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_world, int max_tokens,
                int max_hidden, const void* const* partials, int world, int tokens, int hidden,
                const void* residual, const void* weight, float eps, const void* residual_out,
                const void* norm_out, arrms_plan_t* plan) {
@@ -315,9 +329,9 @@ int arrms_plan(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
     return ARRMS_OK;
 }
 
-int arrms_plan_reduce(int cu_count, const arrms_tuning_t* tuning, int max_world, int max_tokens, int max_hidden,
-                      const void* const* partials, int world, int tokens, int hidden, const void* reduced,
-                      arrms_plan_t* plan) {
+int plan_reduce(int cu_count, const arrms_tuning_t* tuning, int max_world, int max_tokens, int max_hidden,
+                const void* const* partials, int world, int tokens, int hidden, const void* reduced,
+                arrms_plan_t* plan) {
     if (!plan) return ARRMS_ERR_INVALID_ARG;
     memset(plan, 0, sizeof *plan);
     if (cu_count < 1 || max_world < 1 || max_world > ARRMS_MAX_WORLD || max_tokens < 0 || max_hidden < 1 ||
@@ -376,6 +390,27 @@ int arrms_plan_reduce(int cu_count, const arrms_tuning_t* tuning, int max_world,
     }
     finish_vector_plan(tuning, plan, k);
     return ARRMS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int arrms_plan(int cu_count, int variant, const arrms_tuning_t* tuning, int max_world, int max_tokens,
+               int max_hidden, const void* const* partials, int world, int tokens, int hidden,
+               const void* residual, const void* weight, float eps, const void* residual_out,
+               const void* norm_out, arrms_plan_t* plan) {
+    return check_grid(plan_fused(cu_count, variant, tuning, max_world, max_tokens, max_hidden, partials, world,
+                                 tokens, hidden, residual, weight, eps, residual_out, norm_out, plan),
+                      plan);
+}
+
+int arrms_plan_reduce(int cu_count, const arrms_tuning_t* tuning, int max_world, int max_tokens, int max_hidden,
+                      const void* const* partials, int world, int tokens, int hidden, const void* reduced,
+                      arrms_plan_t* plan) {
+    return check_grid(plan_reduce(cu_count, tuning, max_world, max_tokens, max_hidden, partials, world, tokens,
+                                  hidden, reduced, plan),
+                      plan);
 }
 
 int arrms_reduce(arrms_handle_t h, const void* const* partials, int world, int tokens, int hidden, void* reduced,

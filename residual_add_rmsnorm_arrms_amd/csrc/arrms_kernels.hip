@@ -52,13 +52,13 @@ __global__ void __launch_bounds__((row_max_threads<W, VPT>())) row_kernel(const 
     const int nvec = static_cast<int>(a.shape & 0xffffu);
     const int tpr = static_cast<int>((a.shape >> 16) & 127u) * 16;
     const int rpb_log2 = static_cast<int>((a.shape >> 23) & 7u);
-    const int blocks = (a.tokens + (1 << rpb_log2) - 1) >> rpb_log2;
+    const int blocks = static_cast<int>((static_cast<unsigned>(a.tokens) + (1u << rpb_log2) - 1u) >> rpb_log2);
     const int block = logical_block(a.xcd_chunk, blocks);
     if (block < 0) return;  // padding workgroup of the XCD mapping (whole workgroup)
     const int tid = threadIdx.x;
     const int row_in_block = tid / tpr;
     const int lane = tid - row_in_block * tpr;
-    const int row = (block << rpb_log2) + row_in_block;
+    const long long row = (static_cast<long long>(block) << rpb_log2) + row_in_block;
     const bool row_ok = row < a.tokens;
     const size_t base = static_cast<size_t>(row_ok ? row : 0) * static_cast<size_t>(nvec);
 

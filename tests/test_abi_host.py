@@ -157,6 +157,28 @@ def test_forced_variant_unsupported():
     assert plan(8, 10, 2048, variant=A.ARRMS_VARIANT_ROW, tuning=t)[0] == A.ARRMS_ERR_UNSUPPORTED  # registers
 
 
+@pytest.mark.parametrize("T,H", [(2 ** 24, 8), (2 ** 24 - 3, 64), (2 ** 22 + 1, 2048), (2 ** 31 - 1, 8),
+                                 (2 ** 31 - 1, 2048)])
+def test_huge_token_counts(T, H):
+    """Block counts are computed without int overflow; a plan whose grid would exceed
+    2^32 work-items (the launch limit) is refused as unsupported, never truncated."""
+    lim = dict(max_world=8, max_tokens=2 ** 31 - 1, max_hidden=65536)
+    for variant in (A.ARRMS_VARIANT_AUTO, A.ARRMS_VARIANT_ROW, A.ARRMS_VARIANT_SCALAR):
+        rc, p = plan(4, T, H, variant=variant, lim=lim)
+        assert rc in (A.ARRMS_OK, A.ARRMS_ERR_UNSUPPORTED), (variant, rc)
+        if rc == A.ARRMS_ERR_UNSUPPORTED:
+            assert T * min(H, 64) > 2 ** 32 // 256, (T, H, variant)   # only refused when genuinely too big
+            continue
+        assert p["grid"] * p["block"] <= 2 ** 32 - 1
+        assert p["blocks"] > 0 and p["blocks"] * p["rows_per_block"] >= T
+        assert (p["blocks"] - 1) * p["rows_per_block"] < T
+    rc, p = A.arrms_plan_reduce(CU, None, 8, 2 ** 31 - 1, 65536, [BASE + i * 2 ** 44 for i in range(4)], 4, T, H,
+                                BASE + 5 * 2 ** 44)
+    assert rc in (A.ARRMS_OK, A.ARRMS_ERR_UNSUPPORTED)
+    if rc == A.ARRMS_OK:
+        assert p["grid"] * p["block"] <= 2 ** 32 - 1 and p["blocks"] * 256 * 8 * p["vec_per_thread"] >= T * H
+
+
 def test_tokens_zero_is_ok_and_plans_nothing():
     rc, p = A.arrms_plan(CU, 0, None, 4, 10, 2048, None, 4, 0, 2048, 0, 0, 1e-6, 0, 0)
     assert rc == A.ARRMS_OK and p["grid"] == 0
