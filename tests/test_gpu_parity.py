@@ -102,6 +102,16 @@ def test_scalar_spans(W, T, H, inplace):
     assert plan["block"] == min(1024, -(-(-(-H // 8)) // 64) * 64)
 
 
+# The largest hidden size (ARRMS_MAX_HIDDEN) and the largest world size together,
+# on the vector variants the planner can pick for them.
+@pytest.mark.parametrize("W,T,H,variant", [(16, 3, 65536, AUTO), (8, 5, 65536, SPLITH), (16, 2, 65528, SPLITH),
+                                           (8, 4, 16384, ROW), (16, 9, 4096, ROW)])
+def test_largest_sizes(W, T, H, variant):
+    plan, _ = parity(W, T, H, variant=variant, seed=H + W)
+    if variant != AUTO:
+        assert plan["variant"] == variant
+
+
 def _row_tunings(W, H):
     nvec = H // 8
     out = []
