@@ -225,11 +225,12 @@ class FusedReduceResidualRMSNorm:
         if rc != ARRMS_OK:
             raise ArrmsError(rc, "arrms_set_tuning")
 
-    @staticmethod
-    def _check(t, name, shape=None):
+    def _check(self, t, name, shape=None):
         import torch
         if t.dtype != torch.bfloat16 or not t.is_cuda:
             raise TypeError("%s must be a bfloat16 GPU tensor" % name)
+        if t.device.index != self.device:
+            raise ValueError("%s is on cuda:%s, the handle on cuda:%d" % (name, t.device.index, self.device))
         if not t.is_contiguous():
             raise ValueError("%s must be contiguous" % name)
         if shape is not None and tuple(t.shape) != tuple(shape):
