@@ -204,6 +204,10 @@ class FusedReduceResidualRMSNorm:
     ``op(partials, residual, weight, eps, residual_out=None, norm_out=None)`` enqueues
     the fused call on torch's current stream and returns (residual_out, norm_out).
     ``partials`` is a [W, T, H] tensor or a sequence of W [T, H] tensors.
+
+    One handle serves one call at a time (the split-H variant uses the handle's
+    workspace): calls on the same stream are ordered by it, but calls on different
+    streams must not overlap.  Use one operator per stream for concurrent streams.
     """
 
     def __init__(self, max_world: int, max_tokens: int, max_hidden: int, device: Optional[int] = None):
