@@ -584,6 +584,37 @@ def main():
                     name, t, g * 1e3, b / (g * 1e-3) / 1e9, p["grid"], p["block"], p["kernels"]))
         op.set_variant(A.ARRMS_VARIANT_AUTO)
 
+    # ---- where split-H pays: long rows (W=8 H=8192, 180 KB of traffic per row) at
+    # decode token counts, row vs split-H vs the automatic choice, HIP-graph replay
+    # (GPU time per call; 10 rotating sets of 128 rows, 230 MB)
+    splith_regime = []
+    if not args.no_sweep:
+        lw = synth.WORKLOADS["large_hidden"].with_(tokens=128)
+        lx, lr, lwt = synth.make_inputs(lw)
+        lpool = Pool(torch, lx, lr, lwt, rows=128)
+        del lx, lr
+        lop = A.FusedReduceResidualRMSNorm(max_world=lw.world, max_tokens=128, max_hidden=lw.hidden, device=0)
+        for t in (1, 4, 16, 64, 128):
+            row = {"W": lw.world, "H": lw.hidden, "T": t}
+            for v, name in ((A.ARRMS_VARIANT_AUTO, "auto"), (A.ARRMS_VARIANT_ROW, "row"),
+                            (A.ARRMS_VARIANT_SPLITH, "splith")):
+                lop.set_variant(v)
+                c = Caller(A, lop.handle, lpool.sets(t), lw.world, t, lw.hidden, lpool.weight.data_ptr(), lw.eps,
+                           stream)
+                p = lop.plan(lpool.slot[0, :lw.world, :t], lpool.slot[0, lw.world, :t], lpool.weight, lw.eps,
+                             lpool.slot[0, lw.world + 1, :t], lpool.slot[0, lw.world + 2, :t])
+                for _ in range(20):
+                    c()
+                row["us_graph_" + name] = time_graph(torch, c, 50, 10) * 1e3
+                if name == "auto":
+                    row["auto_variant"] = {1: "row", 2: "splith", 3: "scalar"}[p["variant"]]
+            lop.set_variant(A.ARRMS_VARIANT_AUTO)
+            splith_regime.append(row)
+            log("W=8 H=8192 T=%3d graph replay: row %.2f us, split-H %.2f us, auto (%s) %.2f us" % (
+                t, row["us_graph_row"], row["us_graph_splith"], row["auto_variant"], row["us_graph_auto"]))
+        lop.close()
+        del lpool
+
     floor_us = launch_floor_graph_us(torch)
     log("launch floor (one-element kernel, graph replay): %.2f us" % floor_us)
     copy = copy_context(torch, 512 * 2 ** 20)
@@ -634,6 +665,7 @@ def main():
         "copy_context": copy,
         "copy_same_bytes": copy_same,
         "variants": variants,
+        "splith_regime": splith_regime,
         "launch_floor_graph_us": floor_us,
         "device": {"name": props.name, "compute_units": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", None), "memory_GiB": props.total_memory / 2 ** 30},
