@@ -3,6 +3,8 @@
 offsets (16-byte vector paths and the element-wise paths), in-place residual, and
 the rank sum alone.  Every element is compared, to the parity bar of
 tests/gpu_util.py."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -45,7 +47,8 @@ def _cases(n, seed):
     return out
 
 
-CASES = _cases(64, 2024)
+# ARRMS_RANDOM_CASES / ARRMS_RANDOM_SEED scale the sweep up for a longer stress run.
+CASES = _cases(int(os.environ.get("ARRMS_RANDOM_CASES", "64")), int(os.environ.get("ARRMS_RANDOM_SEED", "2024")))
 
 
 def _placed(t, off_bytes):
