@@ -35,7 +35,7 @@ static int fail(const char* what, int i) {
 int main(int argc, char** argv) {
     const int iters = argc > 1 ? atoi(argv[1]) : 200000;
     const int worlds[] = {-1, 0, 1, 2, 3, 4, 5, 8, 9, 12, 16, 17};
-    const int tokens[] = {-5, 0, 1, 2, 3, 16, 17, 64, 255, 256, 1000, 4096, 16383, 100000};
+    const int tokens[] = {-5, 0, 1, 2, 3, 16, 17, 64, 255, 256, 1000, 4096, 16383, 100000, 1 << 24, 0x7fffffff};
     const int hiddens[] = {-1, 0, 1, 3, 8, 64, 128, 1000, 1001, 2048, 5120, 8192, 16384, 16392, 24576, 65536, 65537};
     const int tvpt[] = {0, 0, 0, 1, 2, 3, 4, 8};
     const int ttpr[] = {0, 0, 0, 16, 32, 48, 64, 128, 256, 320, 512, 1024, 2048};
@@ -44,8 +44,9 @@ int main(int argc, char** argv) {
     const int txcd[] = {-2, -1, -1, 0, 1, 7, 64, 1 << 29};
     const int offs[] = {0, 0, 0, 0, 2, 1, 16, 8};
     for (int i = 0; i < iters; ++i) {
-        const int W = pick(worlds, 12), T = pick(tokens, 14), H = pick(hiddens, 17);
-        const int maxw = 1 + (int)(next() % 16), maxt = (int)(next() % 20000), maxh = 1 + (int)(next() % 65536);
+        const int W = pick(worlds, 12), T = pick(tokens, 16), H = pick(hiddens, 17);
+        const int maxw = 1 + (int)(next() % 16), maxh = 1 + (int)(next() % 65536);
+        const int maxt = (next() % 4) ? (int)(next() % 20000) : 0x7fffffff;
         const int cu = (next() % 8) ? 256 : (int)(next() % 300);
         const int trpb[] = {0, 0, 0, 1, 2, 3, 4, 8, 64, 128};
         arrms_tuning_t tun = {pick(tvpt, 8), pick(ttpr, 13), pick(tblk, 7), pick(tspl, 6), pick(txcd, 8), pick(trpb, 10)};
@@ -64,6 +65,7 @@ int main(int argc, char** argv) {
         const int rc = arrms_plan(cu, variant, tp, maxw, maxt, maxh, parts, W, T, H, res, w, eps, ro, no, &p);
         if (rc == ARRMS_OK && T > 0 && p.grid > 0) {
             if (p.blocks > p.grid || p.block < 64 || p.block > 1024 || p.block % 64) return fail("shape", i);
+            if ((long long)p.grid * p.block > 0xffffffffLL) return fail("grid limit", i);
             if (p.variant == ARRMS_VARIANT_ROW) {
                 if ((long)p.blocks * p.rows_per_block < T) return fail("row cover", i);
                 if ((long)p.threads_per_row * p.vec_per_thread < H / 8) return fail("row width", i);
@@ -82,6 +84,7 @@ int main(int argc, char** argv) {
         const int rc2 = arrms_plan_reduce(cu, tp, maxw, maxt, maxh, parts, W, T, H, no, &p);
         if (rc2 == ARRMS_OK && T > 0 && p.grid > 0) {
             const long long count = (long long)T * H;
+            if ((long long)p.grid * p.block > 0xffffffffLL) return fail("reduce grid limit", i);
             if (p.variant == ARRMS_VARIANT_REDUCE) {
                 if ((long long)p.blocks * p.block * p.vec_per_thread < count / 8) return fail("reduce cover", i);
             } else if (p.variant != ARRMS_VARIANT_REDUCE_SCALAR) {
