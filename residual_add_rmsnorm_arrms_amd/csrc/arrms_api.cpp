@@ -111,7 +111,7 @@ void finish_vector_plan(const arrms_tuning_t* t, arrms_plan_t* p, int auto_chunk
 // (a 5-wave group for H=5120 loses about 4% to an 8-wave group with idle
 // lanes), and the best groups hold 256 to 512 lanes.  So: the fewest vectors
 // per lane whose power-of-two row group is at most 512 lanes.
-int plan_row(int world, int tokens, int hidden, const arrms_tuning_t* t, arrms_plan_t* p) {
+int plan_row(int cu_count, int world, int tokens, int hidden, const arrms_tuning_t* t, arrms_plan_t* p) {
     const int nvec = hidden / 8;
     const int we = world_extent(world);
     int best_vpt = 0, best_tpr = 0;
@@ -127,6 +127,21 @@ int plan_row(int world, int tokens, int hidden, const arrms_tuning_t* t, arrms_p
         }
     }
     if (!best_vpt) return ARRMS_ERR_UNSUPPORTED;
+    // One rank (no rank sum, W = 1): at one vector per input a lane keeps only 32
+    // bytes of HBM reads in flight, too few at full occupancy to cover the memory
+    // latency.  Rows of 512..2048 elements therefore take four vectors per lane in
+    // sub-wave row groups, when that still leaves two workgroups per compute unit
+    // (measured on MI355X at H = 512, 1024, 2048 and T = 2048..16384: 4-14 % faster;
+    // with fewer workgroups it is slower, and at W >= 2 it wins and loses by shape).
+    const bool layout_tuned = t && (t->vec_per_thread || t->threads_per_row);
+    if (!layout_tuned && world == 1 && nvec >= 64 && nvec <= 256) {
+        const int tpr4 = pow2_threads((nvec + 3) / 4);
+        const long blocks4 = (static_cast<long>(tokens) + 256 / tpr4 - 1) / (256 / tpr4);
+        if (blocks4 >= 2L * cu_count) {
+            best_vpt = 4;
+            best_tpr = tpr4;
+        }
+    }
     int rpb = best_tpr < 256 ? 256 / best_tpr : 1;
     while (rpb > 1 && best_tpr * rpb > row_max_threads(world, best_vpt)) rpb /= 2;
     if (t && t->rows_per_block) {
@@ -302,7 +317,7 @@ int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
             return ARRMS_OK;
         case ARRMS_VARIANT_ROW:
             if (!vector_ok || hidden > ARRMS_ROW_MAX_HIDDEN) return ARRMS_ERR_UNSUPPORTED;
-            return plan_row(world, tokens, hidden, tuning, plan);
+            return plan_row(cu_count, world, tokens, hidden, tuning, plan);
         case ARRMS_VARIANT_SPLITH:
             if (!vector_ok) return ARRMS_ERR_UNSUPPORTED;
             return plan_splith(cu_count, max_hidden, world, tokens, hidden, tuning, plan);
@@ -320,7 +335,7 @@ int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
         if (rc == ARRMS_OK || hidden > ARRMS_ROW_MAX_HIDDEN) return rc;
         memset(plan, 0, sizeof *plan);
     }
-    if (plan_row(world, tokens, hidden, tuning, plan) == ARRMS_OK) return ARRMS_OK;
+    if (plan_row(cu_count, world, tokens, hidden, tuning, plan) == ARRMS_OK) return ARRMS_OK;
     // A row the row kernels cannot hold in registers: split it, else go element-wise.
     memset(plan, 0, sizeof *plan);
     if (plan_splith(cu_count, max_hidden, world, tokens, hidden, tuning, plan) == ARRMS_OK) return ARRMS_OK;

@@ -265,6 +265,12 @@ def test_create_rejects_bad_limits():
     (4, 16, 2048, A.ARRMS_VARIANT_ROW, 1, 256, 0),         # decode, small rows: one kernel
     (8, 1, 8192, A.ARRMS_VARIANT_SPLITH, 1, 64, 0),        # decode, large rows: split over CUs
     (8, 128, 8192, A.ARRMS_VARIANT_ROW, 2, 512, 16),
+    (1, 4096, 2048, A.ARRMS_VARIANT_ROW, 4, 64, 32),       # one rank, short rows: 4 vectors per lane
+    (1, 8192, 1024, A.ARRMS_VARIANT_ROW, 4, 32, 32),
+    (1, 16384, 512, A.ARRMS_VARIANT_ROW, 4, 16, 32),
+    (1, 4096, 512, A.ARRMS_VARIANT_ROW, 1, 64, 128),       # ... unless fewer than 2 workgroups per CU
+    (1, 1024, 2048, A.ARRMS_VARIANT_ROW, 1, 256, 128),
+    (2, 8192, 1024, A.ARRMS_VARIANT_ROW, 1, 128, 128),     # two ranks keep one vector per lane
 ])
 def test_measured_automatic_choices(W, T, H, variant, vpt, tpr, k):
     """The automatic choices the MI355X measurements led to (speed only; results are

@@ -112,6 +112,14 @@ def test_largest_sizes(W, T, H, variant):
         assert plan["variant"] == variant
 
 
+# One rank with short rows takes four vectors per lane in sub-wave row groups once
+# there are enough rows (automatic plan); ragged T and a non-power-of-two row.
+@pytest.mark.parametrize("T,H", [(4096, 2048), (8192, 1024), (16384, 512), (4097, 1536), (2049, 2048)])
+def test_one_rank_short_rows(T, H):
+    plan, _ = parity(1, T, H, seed=T + H)
+    assert plan["variant"] == ROW and plan["vec_per_thread"] == 4 and plan["threads_per_row"] <= 64
+
+
 def _row_tunings(W, H):
     nvec = H // 8
     out = []
