@@ -58,8 +58,6 @@ TOKENS = [1, 2, 3, 15, 16, 17, 63, 64, 127, 128, 255, 256, 257, 1024, 4096, 1638
 @pytest.mark.parametrize("T", TOKENS)
 @pytest.mark.parametrize("variant", [AUTO, ROW, SPLITH, SCALAR])
 def test_token_sweep(T, variant):
-    if variant == SCALAR and T > 1024:
-        pytest.skip("scalar variant covered up to T=1024")
     plan, _ = parity(4, T, 2048, variant=variant, seed=T)
     if variant != AUTO:
         assert plan["variant"] == variant
