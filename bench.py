@@ -389,6 +389,180 @@ def traffic_record(wl):
     return rec
 
 
+class Ctx:
+    """What the optional benchmark sections share: the prefill pool and its handle."""
+
+    def __init__(self, torch, A, synth, op, pool, W, H, eps, stream):
+        self.torch, self.A, self.synth, self.op, self.pool = torch, A, synth, op, pool
+        self.W, self.H, self.eps, self.stream = W, H, eps, stream
+
+    def caller(self, t):
+        return Caller(self.A, self.op.handle, self.pool.sets(t), self.W, t, self.H, self.pool.weight.data_ptr(),
+                      self.eps, self.stream)
+
+    def plan(self, t):
+        s, W = self.pool.slot, self.W
+        return self.op.plan(s[0, :W, :t], s[0, W, :t], self.pool.weight, self.eps, s[0, W + 1, :t], s[0, W + 2, :t])
+
+
+VARIANT_NAMES = {1: "row", 2: "splith", 3: "scalar"}
+
+
+def sweep_tokens(ctx):
+    """Sweep over T: back-to-back, per-launch, isolated and graph replay."""
+    torch, W, H = ctx.torch, ctx.W, ctx.H
+    sweep = []
+    for t in SWEEP_T:
+        c = ctx.caller(t)
+        p = ctx.plan(t)
+        for _ in range(100):
+            c()
+        k = 2000 if t <= 1024 else 1000
+        wall, gpu = time_back_to_back(torch, c, k)
+        d = time_per_launch(torch, c, 300)
+        iso = time_isolated(torch, c, 100)
+        gr = time_graph(torch, c, 100, 10)
+        b = algorithmic_bytes(W, t, H)
+        row = {"T": t, "variant": VARIANT_NAMES[p["variant"]], "grid": p["grid"],
+               "block": p["block"], "bytes": b,
+               "us_back_to_back_wall": wall * 1e3, "us_back_to_back_gpu": gpu * 1e3,
+               "us_event_pair_p50": pct(d, 50) * 1e3, "us_event_pair_p90": pct(d, 90) * 1e3,
+               "us_event_pair_p99": pct(d, 99) * 1e3,
+               "us_isolated_p50": pct(iso, 50) * 1e3, "us_graph_replay": gr * 1e3,
+               "GB_s_back_to_back": b / (gpu * 1e-3) / 1e9,
+               "GB_s_graph": b / (gr * 1e-3) / 1e9}
+        row["frac_peak_back_to_back"] = row["GB_s_back_to_back"] / HBM_PEAK_GBS
+        sweep.append(row)
+        log("T=%5d %-6s b2b %.2f us (%.0f GB/s, %.1f%%), event pair p50 %.2f us, isolated %.2f us, "
+            "graph %.2f us" % (t, row["variant"], row["us_back_to_back_gpu"], row["GB_s_back_to_back"],
+                               100 * row["frac_peak_back_to_back"], row["us_event_pair_p50"],
+                               row["us_isolated_p50"], row["us_graph_replay"]))
+    return sweep
+
+
+def fixed_and_streaming(ctx):
+    """Per-call fixed time and streaming rate: least-squares line through the
+    back-to-back GPU time at T = 4096, 8192, 16384 (same kernel, same layout)."""
+    pts = []
+    for t in FIT_T:
+        c = ctx.caller(t)
+        for _ in range(50):
+            c()
+        _, g = time_back_to_back(ctx.torch, c, 500)
+        pts.append((t, g * 1e3))
+    n = len(pts)
+    mt = sum(p[0] for p in pts) / n
+    mu = sum(p[1] for p in pts) / n
+    slope = sum((p[0] - mt) * (p[1] - mu) for p in pts) / sum((p[0] - mt) ** 2 for p in pts)
+    icpt = mu - slope * mt
+    row_bytes = 2 * ctx.H * (ctx.W + 3)
+    fit = {"points_us": [{"T": t, "us": u} for t, u in pts], "fixed_us_per_call": icpt,
+           "us_per_row": slope, "streaming_GB_s": row_bytes / (slope * 1e-6) / 1e9,
+           "streaming_frac_of_peak": row_bytes / (slope * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    log("fit over T=%s: fixed %.2f us per call, streaming %.0f GB/s (%.1f%% of peak)" % (
+        FIT_T, icpt, fit["streaming_GB_s"], 100 * fit["streaming_frac_of_peak"]))
+    return fit
+
+
+def fusion_and_rank_sum(ctx, T, nbytes, fused_ms):
+    """The page's two-stage form (rank sum kernel, then the epilogue as a one-rank fused
+    call through a BF16 `reduced` tensor) against the fused call; then the rank sum
+    alone over sizes and W (reads W partials, writes reduced)."""
+    torch, A, op, pool, W, H = ctx.torch, ctx.A, ctx.op, ctx.pool, ctx.W, ctx.H
+    red_pool = torch.empty((POOL_SLOTS, pool.T, H), dtype=torch.bfloat16, device="cuda")
+    rcall = ReduceCaller(A, op.handle, pool, W, T, red_pool.data_ptr(), ctx.stream)
+    per_slot = len(pool.sets(T)) // POOL_SLOTS
+    epi_sets = [([pool.reduced_ptr(red_pool.data_ptr(), T, i // POOL_SLOTS, i % POOL_SLOTS)], st[1], st[2], st[3])
+                for i, st in enumerate(pool.sets(T))]
+    assert len(epi_sets) == per_slot * POOL_SLOTS
+    ecall = Caller(A, op.handle, epi_sets, 1, T, H, pool.weight.data_ptr(), ctx.eps, ctx.stream)
+
+    def two_stage():
+        rcall()
+        ecall()
+    for _ in range(50):
+        two_stage()
+    _, ts_ms = time_back_to_back(torch, two_stage, 1000)
+    _, red_ms = time_back_to_back(torch, rcall, 1000)
+    _, epi_ms = time_back_to_back(torch, ecall, 1000)
+    ts_bytes = nbytes + 2 * 2 * T * H  # plus writing and re-reading `reduced`
+    fusion = {"workload": "W=%d T=%d H=%d" % (W, T, H), "fused_us": fused_ms * 1e3, "two_stage_us": ts_ms * 1e3,
+              "reduce_kernel_us": red_ms * 1e3, "epilogue_kernel_us": epi_ms * 1e3,
+              "two_stage_bytes": ts_bytes, "fused_bytes": nbytes,
+              "fused_speedup": ts_ms / fused_ms}
+    log("fusion: fused %.2f us vs two-stage %.2f us (reduce %.2f + epilogue %.2f): %.2fx" % (
+        fused_ms * 1e3, ts_ms * 1e3, red_ms * 1e3, epi_ms * 1e3, ts_ms / fused_ms))
+    reduce_sweep = []
+    for w_ in (2, 4, 8):
+        for t in (16, 256, 4096):
+            c = ReduceCaller(A, op.handle, pool, w_, t, red_pool.data_ptr(), ctx.stream)
+            for _ in range(50):
+                c()
+            _, ms = time_back_to_back(torch, c, 1000)
+            b = 2 * t * H * (w_ + 1)
+            reduce_sweep.append({"W": w_, "T": t, "H": H, "bytes": b, "us": ms * 1e3,
+                                 "GB_s": b / (ms * 1e-3) / 1e9})
+            log("reduce only W=%d T=%5d: %.2f us, %.0f GB/s" % (w_, t, ms * 1e3, b / (ms * 1e-3) / 1e9))
+    del red_pool
+    return fusion, reduce_sweep
+
+
+def forced_variants(ctx):
+    """Each variant forced on the same shapes (the automatic choice is one of them)."""
+    A, op = ctx.A, ctx.op
+    variants = []
+    for v in (A.ARRMS_VARIANT_ROW, A.ARRMS_VARIANT_SPLITH, A.ARRMS_VARIANT_SCALAR):
+        name = VARIANT_NAMES[v]
+        op.set_variant(v)
+        for t in (1, 16, 128, 4096):
+            c = ctx.caller(t)
+            p = ctx.plan(t)
+            for _ in range(50):
+                c()
+            _, g = time_back_to_back(ctx.torch, c, 1000 if t <= 128 else 300)
+            b = algorithmic_bytes(ctx.W, t, ctx.H)
+            variants.append({"variant": name, "T": t, "grid": p["grid"], "block": p["block"],
+                             "kernels": p["kernels"], "us_back_to_back_gpu": g * 1e3,
+                             "GB_s": b / (g * 1e-3) / 1e9})
+            log("variant %-6s T=%5d: %.2f us (%.0f GB/s), grid %d x %d, %d kernel(s)" % (
+                name, t, g * 1e3, b / (g * 1e-3) / 1e9, p["grid"], p["block"], p["kernels"]))
+    op.set_variant(A.ARRMS_VARIANT_AUTO)
+    return variants
+
+
+def splith_crossover(ctx):
+    """Where split-H pays: long rows (W=8 H=8192, 180 KB of traffic per row) at decode
+    token counts, row vs split-H vs the automatic choice, HIP-graph replay (GPU time per
+    call; 10 rotating sets of 128 rows, 230 MB)."""
+    torch, A = ctx.torch, ctx.A
+    lw = ctx.synth.WORKLOADS["large_hidden"].with_(tokens=128)
+    lx, lr, lwt = ctx.synth.make_inputs(lw)
+    lpool = Pool(torch, lx, lr, lwt, rows=128)
+    del lx, lr
+    lop = A.FusedReduceResidualRMSNorm(max_world=lw.world, max_tokens=128, max_hidden=lw.hidden, device=0)
+    lctx = Ctx(torch, A, ctx.synth, lop, lpool, lw.world, lw.hidden, lw.eps, ctx.stream)
+    out = []
+    for t in (1, 4, 16, 64, 128):
+        row = {"W": lw.world, "H": lw.hidden, "T": t}
+        for v, name in ((A.ARRMS_VARIANT_AUTO, "auto"), (A.ARRMS_VARIANT_ROW, "row"),
+                        (A.ARRMS_VARIANT_SPLITH, "splith")):
+            lop.set_variant(v)
+            c = lctx.caller(t)
+            p = lctx.plan(t)
+            for _ in range(20):
+                c()
+            row["us_graph_" + name] = time_graph(torch, c, 50, 10) * 1e3
+            if name == "auto":
+                row["auto_variant"] = VARIANT_NAMES[p["variant"]]
+        lop.set_variant(A.ARRMS_VARIANT_AUTO)
+        out.append(row)
+        log("W=8 H=8192 T=%3d graph replay: row %.2f us, split-H %.2f us, auto (%s) %.2f us" % (
+            t, row["us_graph_row"], row["us_graph_splith"], row["auto_variant"], row["us_graph_auto"]))
+    lop.close()
+    del lpool
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -469,151 +643,14 @@ def main():
                   "elements": int(ro.size)}
         log("parity of the timed configuration vs oracle: %s" % parity)
 
-    # ---- sweep over T: back-to-back, per-launch, isolated and graph replay
-    sweep = []
+    sweep, fit, fusion, reduce_sweep, variants, splith_regime = [], None, None, [], [], []
     if not args.no_sweep:
-        for t in SWEEP_T:
-            c = caller(t)
-            p = op.plan(pool.slot[0, :W, :t], pool.slot[0, W, :t], pool.weight, eps, pool.slot[0, W + 1, :t],
-                        pool.slot[0, W + 2, :t])
-            for _ in range(100):
-                c()
-            k = 2000 if t <= 1024 else 1000
-            wall, gpu = time_back_to_back(torch, c, k)
-            d = time_per_launch(torch, c, 300)
-            iso = time_isolated(torch, c, 100)
-            gr = time_graph(torch, c, 100, 10)
-            b = algorithmic_bytes(W, t, H)
-            row = {"T": t, "variant": {1: "row", 2: "splith", 3: "scalar"}[p["variant"]], "grid": p["grid"],
-                   "block": p["block"], "bytes": b,
-                   "us_back_to_back_wall": wall * 1e3, "us_back_to_back_gpu": gpu * 1e3,
-                   "us_event_pair_p50": pct(d, 50) * 1e3, "us_event_pair_p90": pct(d, 90) * 1e3,
-                   "us_event_pair_p99": pct(d, 99) * 1e3,
-                   "us_isolated_p50": pct(iso, 50) * 1e3, "us_graph_replay": gr * 1e3,
-                   "GB_s_back_to_back": b / (gpu * 1e-3) / 1e9,
-                   "GB_s_graph": b / (gr * 1e-3) / 1e9}
-            row["frac_peak_back_to_back"] = row["GB_s_back_to_back"] / HBM_PEAK_GBS
-            sweep.append(row)
-            log("T=%5d %-6s b2b %.2f us (%.0f GB/s, %.1f%%), event pair p50 %.2f us, isolated %.2f us, "
-                "graph %.2f us" % (t, row["variant"], row["us_back_to_back_gpu"], row["GB_s_back_to_back"],
-                                   100 * row["frac_peak_back_to_back"], row["us_event_pair_p50"],
-                                   row["us_isolated_p50"], row["us_graph_replay"]))
-
-    # ---- per-call fixed time and streaming rate: least-squares line through the
-    # back-to-back GPU time at T = 4096, 8192, 16384 (same kernel, same layout)
-    fit = None
-    if not args.no_sweep:
-        pts = []
-        for t in FIT_T:
-            c = caller(t)
-            for _ in range(50):
-                c()
-            _, g = time_back_to_back(torch, c, 500)
-            pts.append((t, g * 1e3))
-        n = len(pts)
-        mt = sum(p[0] for p in pts) / n
-        mu = sum(p[1] for p in pts) / n
-        slope = sum((p[0] - mt) * (p[1] - mu) for p in pts) / sum((p[0] - mt) ** 2 for p in pts)
-        icpt = mu - slope * mt
-        row_bytes = 2 * H * (W + 3)
-        fit = {"points_us": [{"T": t, "us": u} for t, u in pts], "fixed_us_per_call": icpt,
-               "us_per_row": slope, "streaming_GB_s": row_bytes / (slope * 1e-6) / 1e9,
-               "streaming_frac_of_peak": row_bytes / (slope * 1e-6) / 1e9 / HBM_PEAK_GBS}
-        log("fit over T=%s: fixed %.2f us per call, streaming %.0f GB/s (%.1f%% of peak)" % (
-            FIT_T, icpt, fit["streaming_GB_s"], 100 * fit["streaming_frac_of_peak"]))
-
-    # ---- fusion: the page's two-stage form (rank sum kernel, then the epilogue as a
-    # one-rank fused call through a BF16 `reduced` tensor) against the fused call
-    fusion = None
-    reduce_sweep = []
-    if not args.no_sweep:
-        red_pool = torch.empty((POOL_SLOTS, pool.T, H), dtype=torch.bfloat16, device="cuda")
-        rcall = ReduceCaller(A, op.handle, pool, W, T, red_pool.data_ptr(), stream)
-        per_slot = len(pool.sets(T)) // POOL_SLOTS
-        epi_sets = [([pool.reduced_ptr(red_pool.data_ptr(), T, i // POOL_SLOTS, i % POOL_SLOTS)], st[1], st[2], st[3])
-                    for i, st in enumerate(pool.sets(T))]
-        assert len(epi_sets) == per_slot * POOL_SLOTS
-        ecall = Caller(A, op.handle, epi_sets, 1, T, H, pool.weight.data_ptr(), eps, stream)
-
-        def two_stage():
-            rcall()
-            ecall()
-        for _ in range(50):
-            two_stage()
-        _, ts_ms = time_back_to_back(torch, two_stage, 1000)
-        _, red_ms = time_back_to_back(torch, rcall, 1000)
-        _, epi_ms = time_back_to_back(torch, ecall, 1000)
-        ts_bytes = nbytes + 2 * 2 * T * H  # plus writing and re-reading `reduced`
-        fusion = {"workload": "W=%d T=%d H=%d" % (W, T, H), "fused_us": gpu_ms * 1e3, "two_stage_us": ts_ms * 1e3,
-                  "reduce_kernel_us": red_ms * 1e3, "epilogue_kernel_us": epi_ms * 1e3,
-                  "two_stage_bytes": ts_bytes, "fused_bytes": nbytes,
-                  "fused_speedup": ts_ms / gpu_ms}
-        log("fusion: fused %.2f us vs two-stage %.2f us (reduce %.2f + epilogue %.2f): %.2fx" % (
-            gpu_ms * 1e3, ts_ms * 1e3, red_ms * 1e3, epi_ms * 1e3, ts_ms / gpu_ms))
-        # ---- the rank sum alone over sizes and W (reads W partials, writes reduced)
-        for w_ in (2, 4, 8):
-            for t in (16, 256, 4096):
-                c = ReduceCaller(A, op.handle, pool, w_, t, red_pool.data_ptr(), stream)
-                for _ in range(50):
-                    c()
-                _, ms = time_back_to_back(torch, c, 1000)
-                b = 2 * t * H * (w_ + 1)
-                reduce_sweep.append({"W": w_, "T": t, "H": H, "bytes": b, "us": ms * 1e3,
-                                     "GB_s": b / (ms * 1e-3) / 1e9})
-                log("reduce only W=%d T=%5d: %.2f us, %.0f GB/s" % (w_, t, ms * 1e3, b / (ms * 1e-3) / 1e9))
-        del red_pool
-
-    # ---- each variant forced on the same shapes (the automatic choice is one of them)
-    variants = []
-    if not args.no_sweep:
-        names = {A.ARRMS_VARIANT_ROW: "row", A.ARRMS_VARIANT_SPLITH: "splith", A.ARRMS_VARIANT_SCALAR: "scalar"}
-        for v, name in names.items():
-            op.set_variant(v)
-            for t in (1, 16, 128, 4096):
-                c = caller(t)
-                p = op.plan(pool.slot[0, :W, :t], pool.slot[0, W, :t], pool.weight, eps,
-                            pool.slot[0, W + 1, :t], pool.slot[0, W + 2, :t])
-                for _ in range(50):
-                    c()
-                _, g = time_back_to_back(torch, c, 1000 if t <= 128 else 300)
-                b = algorithmic_bytes(W, t, H)
-                variants.append({"variant": name, "T": t, "grid": p["grid"], "block": p["block"],
-                                 "kernels": p["kernels"], "us_back_to_back_gpu": g * 1e3,
-                                 "GB_s": b / (g * 1e-3) / 1e9})
-                log("variant %-6s T=%5d: %.2f us (%.0f GB/s), grid %d x %d, %d kernel(s)" % (
-                    name, t, g * 1e3, b / (g * 1e-3) / 1e9, p["grid"], p["block"], p["kernels"]))
-        op.set_variant(A.ARRMS_VARIANT_AUTO)
-
-    # ---- where split-H pays: long rows (W=8 H=8192, 180 KB of traffic per row) at
-    # decode token counts, row vs split-H vs the automatic choice, HIP-graph replay
-    # (GPU time per call; 10 rotating sets of 128 rows, 230 MB)
-    splith_regime = []
-    if not args.no_sweep:
-        lw = synth.WORKLOADS["large_hidden"].with_(tokens=128)
-        lx, lr, lwt = synth.make_inputs(lw)
-        lpool = Pool(torch, lx, lr, lwt, rows=128)
-        del lx, lr
-        lop = A.FusedReduceResidualRMSNorm(max_world=lw.world, max_tokens=128, max_hidden=lw.hidden, device=0)
-        for t in (1, 4, 16, 64, 128):
-            row = {"W": lw.world, "H": lw.hidden, "T": t}
-            for v, name in ((A.ARRMS_VARIANT_AUTO, "auto"), (A.ARRMS_VARIANT_ROW, "row"),
-                            (A.ARRMS_VARIANT_SPLITH, "splith")):
-                lop.set_variant(v)
-                c = Caller(A, lop.handle, lpool.sets(t), lw.world, t, lw.hidden, lpool.weight.data_ptr(), lw.eps,
-                           stream)
-                p = lop.plan(lpool.slot[0, :lw.world, :t], lpool.slot[0, lw.world, :t], lpool.weight, lw.eps,
-                             lpool.slot[0, lw.world + 1, :t], lpool.slot[0, lw.world + 2, :t])
-                for _ in range(20):
-                    c()
-                row["us_graph_" + name] = time_graph(torch, c, 50, 10) * 1e3
-                if name == "auto":
-                    row["auto_variant"] = {1: "row", 2: "splith", 3: "scalar"}[p["variant"]]
-            lop.set_variant(A.ARRMS_VARIANT_AUTO)
-            splith_regime.append(row)
-            log("W=8 H=8192 T=%3d graph replay: row %.2f us, split-H %.2f us, auto (%s) %.2f us" % (
-                t, row["us_graph_row"], row["us_graph_splith"], row["auto_variant"], row["us_graph_auto"]))
-        lop.close()
-        del lpool
+        ctx = Ctx(torch, A, synth, op, pool, W, H, eps, stream)
+        sweep = sweep_tokens(ctx)
+        fit = fixed_and_streaming(ctx)
+        fusion, reduce_sweep = fusion_and_rank_sum(ctx, T, nbytes, gpu_ms)
+        variants = forced_variants(ctx)
+        splith_regime = splith_crossover(ctx)
 
     floor_us = launch_floor_graph_us(torch)
     log("launch floor (one-element kernel, graph replay): %.2f us" % floor_us)
