@@ -240,14 +240,27 @@ class FusedReduceResidualRMSNorm:
         if shape is not None and tuple(t.shape) != tuple(shape):
             raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
 
+    def _partial_ptrs(self, partials, T, H):
+        """Device pointers of the W partials: a [W, T, H] tensor (checked once, pointers
+        by stride, no per-rank views) or a sequence of W [T, H] tensors."""
+        import torch
+        if isinstance(partials, torch.Tensor) and partials.dim() == 3:
+            if partials.is_contiguous():
+                self._check(partials, "partials", (partials.shape[0], T, H))
+                base, step = partials.data_ptr(), T * H * partials.element_size()
+                return [base + r * step for r in range(partials.shape[0])]
+            partials = partials.unbind(0)  # e.g. a token slice of a larger buffer: each rank's rows contiguous
+        parts = list(partials)
+        for i, p in enumerate(parts):
+            self._check(p, "partials[%d]" % i, (T, H))
+        return [p.data_ptr() for p in parts]
+
     def _args(self, partials, residual, weight, residual_out, norm_out):
         import torch
-        parts = list(partials.unbind(0)) if isinstance(partials, torch.Tensor) and partials.dim() == 3 else list(partials)
         if residual.dim() != 2:
             raise ValueError("residual must be [T, H]")
         T, H = residual.shape
-        for i, p in enumerate(parts):
-            self._check(p, "partials[%d]" % i, (T, H))
+        parts = self._partial_ptrs(partials, T, H)
         self._check(residual, "residual")
         self._check(weight, "weight", (H,))
         if residual_out is None:
@@ -260,7 +273,7 @@ class FusedReduceResidualRMSNorm:
 
     def plan(self, partials, residual, weight, eps, residual_out=None, norm_out=None) -> dict:
         parts, T, H, residual_out, norm_out = self._args(partials, residual, weight, residual_out, norm_out)
-        rc, p = arrms_query_plan(self.handle, [q.data_ptr() for q in parts], len(parts), T, H, residual.data_ptr(),
+        rc, p = arrms_query_plan(self.handle, parts, len(parts), T, H, residual.data_ptr(),
                                  weight.data_ptr(), eps, residual_out.data_ptr(), norm_out.data_ptr())
         if rc != ARRMS_OK:
             raise ArrmsError(rc, "arrms_query_plan")
@@ -270,7 +283,7 @@ class FusedReduceResidualRMSNorm:
         import torch
         parts, T, H, residual_out, norm_out = self._args(partials, residual, weight, residual_out, norm_out)
         s = (stream if stream is not None else torch.cuda.current_stream(self.device)).cuda_stream
-        rc = arrms_fused(self.handle, [q.data_ptr() for q in parts], len(parts), T, H, residual.data_ptr(),
+        rc = arrms_fused(self.handle, parts, len(parts), T, H, residual.data_ptr(),
                          weight.data_ptr(), eps, residual_out.data_ptr(), norm_out.data_ptr(), s)
         if rc != ARRMS_OK:
             raise ArrmsError(rc, "arrms_fused")
@@ -282,15 +295,14 @@ class FusedReduceResidualRMSNorm:
         (for serving loops on static buffers).  The tensors must stay alive and in place;
         the stream is fixed at bind time (torch's current stream by default)."""
         import torch
-        parts, T, H, residual_out, norm_out = self._args(partials, residual, weight, residual_out, norm_out)
+        ptrs, T, H, residual_out, norm_out = self._args(partials, residual, weight, residual_out, norm_out)
         s = (stream if stream is not None else torch.cuda.current_stream(self.device)).cuda_stream
-        ptrs = [q.data_ptr() for q in parts]
-        rc, _ = arrms_query_plan(self.handle, ptrs, len(parts), T, H, residual.data_ptr(), weight.data_ptr(), eps,
+        rc, _ = arrms_query_plan(self.handle, ptrs, len(ptrs), T, H, residual.data_ptr(), weight.data_ptr(), eps,
                                  residual_out.data_ptr(), norm_out.data_ptr())
         if rc != ARRMS_OK:
             raise ArrmsError(rc, "arrms_fused")
-        return BoundCall(self, (parts, residual, weight, residual_out, norm_out),
-                         (ctypes.c_void_p(self.handle), _ptrs(ptrs), len(parts), T, H,
+        return BoundCall(self, (partials, residual, weight, residual_out, norm_out),
+                         (ctypes.c_void_p(self.handle), _ptrs(ptrs), len(ptrs), T, H,
                           ctypes.c_void_p(residual.data_ptr()), ctypes.c_void_p(weight.data_ptr()),
                           ctypes.c_float(eps), ctypes.c_void_p(residual_out.data_ptr()),
                           ctypes.c_void_p(norm_out.data_ptr()), ctypes.c_void_p(s)),
@@ -299,15 +311,14 @@ class FusedReduceResidualRMSNorm:
     def reduce(self, partials, reduced=None, stream=None):
         """reduced = BF16 rank sum of the partials ([W, T, H] or W x [T, H]); returns reduced."""
         import torch
-        parts = list(partials.unbind(0)) if isinstance(partials, torch.Tensor) and partials.dim() == 3 else list(partials)
-        T, H = parts[0].shape
-        for i, p in enumerate(parts):
-            self._check(p, "partials[%d]" % i, (T, H))
+        first = partials[0]
+        T, H = first.shape
+        ptrs = self._partial_ptrs(partials, T, H)
         if reduced is None:
-            reduced = torch.empty_like(parts[0])
+            reduced = torch.empty((T, H), dtype=first.dtype, device=first.device)
         self._check(reduced, "reduced", (T, H))
         s = (stream if stream is not None else torch.cuda.current_stream(self.device)).cuda_stream
-        rc = arrms_reduce(self.handle, [q.data_ptr() for q in parts], len(parts), T, H, reduced.data_ptr(), s)
+        rc = arrms_reduce(self.handle, ptrs, len(ptrs), T, H, reduced.data_ptr(), s)
         if rc != ARRMS_OK:
             raise ArrmsError(rc, "arrms_reduce")
         return reduced

@@ -173,6 +173,21 @@ def test_xcd_mapping(W, T, H, variant, xcd):
 
 
 # ------------------------------------------------------------ semantics and edge cases
+def test_partials_as_a_token_slice_of_a_larger_buffer():
+    """[W, T, H] partials that are a token slice of a [W, T2, H] buffer (not contiguous as a
+    whole, each rank's rows contiguous) go through the per-rank pointer path."""
+    say("case partials token slice")
+    W, T, H = 4, 50, 2048
+    x, res, w = inputs(W, T, H, seed=21)
+    big = torch.zeros((W, T + 30, H), dtype=torch.bfloat16, device="cuda")
+    big[:, 10:10 + T].copy_(x.to("cuda"))
+    xs = big[:, 10:10 + T]
+    assert not xs.is_contiguous()
+    ro, no = op()(xs, res.to("cuda"), w.to("cuda"), 1e-6)
+    torch.cuda.synchronize()
+    assert_parity(synth.bits(ro.cpu()), synth.bits(no.cpu()), reference(x, res, w, 1e-6), "token slice")
+
+
 @pytest.mark.parametrize("variant", [ROW, SPLITH, SCALAR])
 def test_in_place_residual(variant):
     parity(4, 130, 2048, variant=variant, inplace=True, seed=3)
