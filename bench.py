@@ -563,6 +563,116 @@ def splith_crossover(ctx):
     return out
 
 
+# ------------------------------------------------------------ rocprofv3 summaries
+def _short_kernel_name(n: str) -> str:
+    n = n.replace("void arrms::(anonymous namespace)::", "")
+    if n.startswith(("row_kernel", "splith_", "scalar_kernel", "reduce_")):
+        n = n[:n.index("(")] if "(" in n else n
+    return n[:70]
+
+
+def summarize_profiles(run_dir: str, workload: str) -> None:
+    """Write profiles/row_kernel_<workload>.md and profiles/traffic_<workload>.json from
+    the outputs of the three rocprofv3 runs named in them (kernel trace of the
+    benchmark command; FETCH_SIZE and WRITE_SIZE passes), found under run_dir
+    (bench.json, prof_bench/, pmc_fetch/, pmc_write/)."""
+    import collections
+    import csv
+    import synth
+    wl = synth.WORKLOADS[workload]
+    W, T, H = wl.world, wl.tokens, wl.hidden
+    alg = algorithmic_bytes(W, T, H)
+    sha = kernel_source_hash()
+    bench = json.load(open(os.path.join(run_dir, "bench.json")))
+    plan = bench["config"]["plan"]
+    grid_threads = plan["grid"] * plan["block"]
+    flag = "" if workload == "prefill" else " --workload %s" % workload
+    trace = collections.defaultdict(list)
+    for r in csv.DictReader(open(os.path.join(run_dir, "prof_bench", "bench_kernel_trace.csv"))):
+        key = (_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        trace[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    # the headline kernel: the most dispatched library kernel at the headline launch shape
+    kname = max((len(v), k) for k, v in trace.items()
+                if k[1] == grid_threads and k[2] == plan["block"] and "kernel<" in k[0])[1][0]
+    head = trace[(kname, grid_threads, plan["block"])]
+
+    def counter(path):
+        out = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            out[(_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+        return out
+    fetch = counter(os.path.join(run_dir, "pmc_fetch", "fetch_counter_collection.csv"))
+    write = counter(os.path.join(run_dir, "pmc_write", "write_counter_collection.csv"))
+    kkey = (kname, grid_threads)
+    f_raw, w_raw = statistics.mean(fetch[kkey]), statistics.mean(write[kkey])
+    # calibration: the 512 MiB device copy of copy_context (its WRITE_SIZE is 512 MiB)
+    copy_bytes = 512 * 2 ** 20
+    cw = max(v for (k, _), vs in write.items() if "copyBuffer" in k for v in vs
+             if abs(v * 1024 - copy_bytes) < 0.02 * copy_bytes)
+    cf = min((v for (k, _), vs in fetch.items() if "copyBuffer" in k for v in vs),
+             key=lambda v: abs(v * 1024 * 2 - copy_bytes))
+    fscale, wscale = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    fb, wb = f_raw * 1024 * fscale, w_raw * 1024 * wscale
+    cmd_trace = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
+                 "-d gpurun_out/prof_bench -o bench -- python -u bench.py" + flag)
+    cmd_f = ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- "
+             "python -u bench.py%s --no-cpu %s--steps 50 --warmup 5" % (flag, "--no-sweep " if workload == "prefill" else ""))
+    cmd_w = cmd_f.replace("FETCH_SIZE", "WRITE_SIZE").replace("pmc_fetch", "pmc_write").replace("-o fetch", "-o write")
+    base = "%s_w%d_h%d_t%d" % (workload, W, H, T)
+    traffic = {
+        "kernel": kname, "workload": "W=%d T=%d H=%d (%s), launch grid %d x %d" % (W, T, H, workload, plan["grid"],
+                                                                                plan["block"]),
+        "dispatches": len(fetch[kkey]),
+        "fetch_kib_per_dispatch_raw": f_raw, "write_kib_per_dispatch_raw": w_raw,
+        "copy_calibration": {"kernel": "__amd_rocclr_copyBuffer (torch copy_ of 512 MiB bf16)",
+                             "bytes_read": copy_bytes, "bytes_written": copy_bytes, "fetch_kib_raw": cf,
+                             "write_kib_raw": cw, "fetch_scale": fscale, "write_scale": wscale},
+        "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+        "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": (fb + wb) / alg,
+        "kernel_source_sha256_16": sha, "commands": [cmd_f, cmd_w],
+    }
+    json.dump(traffic, open(traffic_file(wl), "w"), indent=1)
+    L = ["# %s on W=%d T=%d H=%d (%s) — rocprofv3 summary\n" % (kname, W, T, H, workload),
+         "GPU: MI355X (gfx950), one GPU.  Kernel source hash (sha256[:16] of the code without comments, as "
+         "bench.py computes it) = `%s`.  Written by `python bench.py --summarize <run dir>%s` from the runs below.\n"
+         % (sha, flag),
+         "## Kernel trace (same command as the benchmark)\n", "```\n%s\n```\n" % cmd_trace]
+    if workload == "prefill":
+        L.append("Dispatches grouped by kernel and launch shape (grid in threads). Every T of the sweep uses "
+                 "`row_kernel<4, 1>` (the headline launch is grid %d x %d threads); the split-H and scalar kernels "
+                 "come from the forced-variant and split-H sections, `reduce_kernel` from the rank-sum sections, "
+                 "`copyBuffer` from the copy references. Shapes with fewer than 3 dispatches are left out.\n"
+                 % (plan["grid"], plan["block"]))
+    else:
+        L.append("Dispatches grouped by kernel and launch shape (grid in threads); the headline launch is `%s`, grid "
+                 "%d x %d threads, and `copyBuffer` comes from the copy references. Shapes with fewer than 3 "
+                 "dispatches are left out.\n" % (kname, plan["grid"], plan["block"]))
+    L += ["| kernel | grid (threads) | block | dispatches | mean us | p50 us | min us | max us |",
+          "|---|---|---|---|---|---|---|---|"]
+    for (k, gs, bs), v in sorted(trace.items(), key=lambda kv: (-len(kv[1]), kv[0])):
+        if len(v) >= 3:
+            L.append("| %s | %d | %d | %d | %.2f | %.2f | %.2f | %.2f |" % (
+                k, gs, bs, len(v), statistics.mean(v) / 1e3, statistics.median(v) / 1e3, min(v) / 1e3,
+                max(v) / 1e3))
+    hm = statistics.mean(head) / 1e3
+    L.append("\nHeadline launch: mean %.2f us over %d dispatches -> %.1f GB/s algorithmic (%d B per launch); "
+             "bench.py reported %.2f us per launch from HIP events over its timed region (%.1f GB/s).\n" % (
+                 hm, len(head), alg / (hm * 1e-6) / 1e9, alg, bench["roofline"]["kernel_mean_us"],
+                 bench["roofline"]["achieved"]))
+    L += ["## HBM traffic (FETCH_SIZE, WRITE_SIZE), one counter per run\n", "```\n%s\n%s\n```\n" % (cmd_f, cmd_w),
+          "Calibration: the 512 MiB device copy in the same runs (`__amd_rocclr_copyBuffer`) reads FETCH_SIZE = "
+          "%.1f KiB and WRITE_SIZE = %.1f KiB per dispatch for 524288 KiB read and written, so FETCH_SIZE is "
+          "scaled by %.4f and WRITE_SIZE by %.4f.\n" % (cf, cw, fscale, wscale),
+          "| counter | raw KiB / dispatch | scaled bytes / launch | algorithmic bytes |", "|---|---|---|---|",
+          "| FETCH_SIZE | %.1f | %.0f | %d (read: W partials + residual + weight) |" % (
+              f_raw, fb, 2 * T * H * (W + 1) + 2 * H),
+          "| WRITE_SIZE | %.1f | %.0f | %d (residual_out + norm_out) |" % (w_raw, wb, 2 * T * H * 2),
+          "\nTotal traffic / algorithmic bytes = %.4f over %d dispatches.\n" % ((fb + wb) / alg, len(fetch[kkey]))]
+    with open(os.path.join(ROOT, "profiles", "row_kernel_%s.md" % base), "w") as f:
+        f.write("\n".join(L) + "\n")
+
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -574,7 +684,12 @@ def main():
     ap.add_argument("--workload", default="prefill", choices=BENCH_WORKLOADS,
                     help="headline workload (the T sweep, fit, fusion, variant and rank-sum sections run "
                          "only for prefill, the metric's W=4 H=2048 shape)")
+    ap.add_argument("--summarize", metavar="RUN_DIR",
+                    help="write the profiles/ summary of the workload from rocprofv3 outputs in RUN_DIR and exit")
     args = ap.parse_args()
+    if args.summarize:
+        summarize_profiles(args.summarize, args.workload)
+        return
     if args.workload != "prefill":
         args.no_sweep = True
 
