@@ -571,7 +571,7 @@ def _short_kernel_name(n: str) -> str:
     return n[:70]
 
 
-def summarize_profiles(run_dir: str, workload: str) -> None:
+def summarize_profiles(run_dir: str, workload: str, out_dir: str = None) -> None:
     """Write profiles/row_kernel_<workload>.md and profiles/traffic_<workload>.json from
     the outputs of the three rocprofv3 runs named in them (kernel trace of the
     benchmark command; FETCH_SIZE and WRITE_SIZE passes), found under run_dir
@@ -631,7 +631,8 @@ def summarize_profiles(run_dir: str, workload: str) -> None:
         "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": (fb + wb) / alg,
         "kernel_source_sha256_16": sha, "commands": [cmd_f, cmd_w],
     }
-    json.dump(traffic, open(traffic_file(wl), "w"), indent=1)
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    json.dump(traffic, open(os.path.join(out_dir, os.path.basename(traffic_file(wl))), "w"), indent=1)
     L = ["# %s on W=%d T=%d H=%d (%s) — rocprofv3 summary\n" % (kname, W, T, H, workload),
          "GPU: MI355X (gfx950), one GPU.  Kernel source hash (sha256[:16] of the code without comments, as "
          "bench.py computes it) = `%s`.  Written by `python bench.py --summarize <run dir>%s` from the runs below.\n"
@@ -668,7 +669,7 @@ def summarize_profiles(run_dir: str, workload: str) -> None:
               f_raw, fb, 2 * T * H * (W + 1) + 2 * H),
           "| WRITE_SIZE | %.1f | %.0f | %d (residual_out + norm_out) |" % (w_raw, wb, 2 * T * H * 2),
           "\nTotal traffic / algorithmic bytes = %.4f over %d dispatches.\n" % ((fb + wb) / alg, len(fetch[kkey]))]
-    with open(os.path.join(ROOT, "profiles", "row_kernel_%s.md" % base), "w") as f:
+    with open(os.path.join(out_dir, "row_kernel_%s.md" % base), "w") as f:
         f.write("\n".join(L) + "\n")
 
 
