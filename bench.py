@@ -530,6 +530,36 @@ def forced_variants(ctx):
     return variants
 
 
+def world_sweep(ctx, T=4096, worlds=(1, 2, 3, 4, 6, 8, 12, 16)):
+    """The fused call at H=2048 T=4096 across rank counts (the shapes of other
+    tensor-parallel degrees): back-to-back GPU time and achieved bandwidth, each W
+    on its own 10-slot rotating pool (automatic plan)."""
+    torch, A, H = ctx.torch, ctx.A, ctx.H
+    out = []
+    for W in worlds:
+        wl = ctx.synth.WORKLOADS["prefill"].with_(world=W, tokens=T, seed=500 + W)
+        x, r, w = ctx.synth.make_inputs(wl)
+        wpool = Pool(torch, x, r, w, rows=T)
+        del x, r
+        wop = A.FusedReduceResidualRMSNorm(max_world=W, max_tokens=T, max_hidden=H, device=0)
+        wctx = Ctx(torch, A, ctx.synth, wop, wpool, W, H, wl.eps, ctx.stream)
+        c = wctx.caller(T)
+        p = wctx.plan(T)
+        for _ in range(30):
+            c()
+        _, g = time_back_to_back(torch, c, 500)
+        b = algorithmic_bytes(W, T, H)
+        out.append({"W": W, "T": T, "H": H, "us": g * 1e3, "GB_s": b / (g * 1e-3) / 1e9,
+                    "frac_of_peak": b / (g * 1e-3) / 1e9 / HBM_PEAK_GBS, "vec_per_thread": p["vec_per_thread"],
+                    "threads_per_row": p["threads_per_row"], "xcd_chunk": p["xcd_chunk"]})
+        log("W=%2d T=%d H=%d: %.2f us, %.0f GB/s (%.1f%%)" % (W, T, H, g * 1e3, b / (g * 1e-3) / 1e9,
+                                                           100 * out[-1]["frac_of_peak"]))
+        wop.close()
+        del wpool
+        torch.cuda.empty_cache()
+    return out
+
+
 def splith_crossover(ctx):
     """Where split-H pays: long rows (W=8 H=8192, 180 KB of traffic per row) at decode
     token counts, row vs split-H vs the automatic choice, HIP-graph replay (GPU time per
@@ -759,7 +789,7 @@ def main():
                   "elements": int(ro.size)}
         log("parity of the timed configuration vs oracle: %s" % parity)
 
-    sweep, fit, fusion, reduce_sweep, variants, splith_regime = [], None, None, [], [], []
+    sweep, fit, fusion, reduce_sweep, variants, splith_regime, worlds = [], None, None, [], [], [], []
     if not args.no_sweep:
         ctx = Ctx(torch, A, synth, op, pool, W, H, eps, stream)
         sweep = sweep_tokens(ctx)
@@ -767,6 +797,7 @@ def main():
         fusion, reduce_sweep = fusion_and_rank_sum(ctx, T, nbytes, gpu_ms)
         variants = forced_variants(ctx)
         splith_regime = splith_crossover(ctx)
+        worlds = world_sweep(ctx)
 
     floor_us = launch_floor_graph_us(torch)
     log("launch floor (one-element kernel, graph replay): %.2f us" % floor_us)
@@ -819,6 +850,7 @@ def main():
         "copy_same_bytes": copy_same,
         "variants": variants,
         "splith_regime": splith_regime,
+        "world_sweep": worlds,
         "launch_floor_graph_us": floor_us,
         "device": {"name": props.name, "compute_units": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", None), "memory_GiB": props.total_memory / 2 ** 30},
