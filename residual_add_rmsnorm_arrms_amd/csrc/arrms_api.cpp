@@ -133,11 +133,19 @@ int plan_row(int cu_count, int world, int tokens, int hidden, const arrms_tuning
     // sub-wave row groups, when that still leaves two workgroups per compute unit
     // (measured on MI355X at H = 512, 1024, 2048 and T = 2048..16384: 4-14 % faster;
     // with fewer workgroups it is slower, and at W >= 2 it wins and loses by shape).
+    // Two ranks (48 bytes in flight per lane) gain the same way, but only while the
+    // four-vector workgroups fit in one round on the CUs: capped at four per CU (these
+    // instances hold 5-6 workgroups per CU) they measured 4-13 % faster at
+    // H = 512..2048 and T = 2048..16384 and never slower; past the cap a second,
+    // partial round made them up to 12 % slower.  Three ranks won at some of these
+    // shapes and lost up to 4 % at others, and W >= 4 loses (8 % at W=4 H=2048
+    // T=4096), so they keep one vector per lane.
     const bool layout_tuned = t && (t->vec_per_thread || t->threads_per_row);
-    if (!layout_tuned && world == 1 && nvec >= 64 && nvec <= 256) {
+    if (!layout_tuned && world <= 2 && nvec >= 64 && nvec <= 256) {
         const int tpr4 = pow2_threads((nvec + 3) / 4);
         const long blocks4 = (static_cast<long>(tokens) + 256 / tpr4 - 1) / (256 / tpr4);
-        if (blocks4 >= 2L * cu_count) {
+        const bool fits = world == 1 || blocks4 <= 4L * cu_count;
+        if (blocks4 >= 2L * cu_count && fits) {
             best_vpt = 4;
             best_tpr = tpr4;
         }

@@ -270,7 +270,11 @@ def test_create_rejects_bad_limits():
     (1, 16384, 512, A.ARRMS_VARIANT_ROW, 4, 16, 32),
     (1, 4096, 512, A.ARRMS_VARIANT_ROW, 1, 64, 128),       # ... unless fewer than 2 workgroups per CU
     (1, 1024, 2048, A.ARRMS_VARIANT_ROW, 1, 256, 128),
-    (2, 8192, 1024, A.ARRMS_VARIANT_ROW, 1, 128, 128),     # two ranks keep one vector per lane
+    (2, 8192, 1024, A.ARRMS_VARIANT_ROW, 4, 32, 32),       # two ranks: four vectors while one round fits
+    (2, 16384, 1024, A.ARRMS_VARIANT_ROW, 1, 128, 128),    # ... not beyond four workgroups per CU
+    (2, 4096, 2048, A.ARRMS_VARIANT_ROW, 4, 64, 32),
+    (3, 2048, 1536, A.ARRMS_VARIANT_ROW, 1, 256, 128),     # three ranks keep one vector per lane
+    (4, 4096, 2048, A.ARRMS_VARIANT_ROW, 1, 256, 64),      # four ranks keep one vector per lane
 ])
 def test_measured_automatic_choices(W, T, H, variant, vpt, tpr, k):
     """The automatic choices the MI355X measurements led to (speed only; results are

@@ -110,11 +110,13 @@ def test_largest_sizes(W, T, H, variant):
         assert plan["variant"] == variant
 
 
-# One rank with short rows takes four vectors per lane in sub-wave row groups once
-# there are enough rows (automatic plan); ragged T and a non-power-of-two row.
-@pytest.mark.parametrize("T,H", [(4096, 2048), (8192, 1024), (16384, 512), (4097, 1536), (2049, 2048)])
-def test_one_rank_short_rows(T, H):
-    plan, _ = parity(1, T, H, seed=T + H)
+# One or two ranks with short rows take four vectors per lane in sub-wave row groups
+# when the automatic plan finds enough rows (ragged T, a non-power-of-two row).
+@pytest.mark.parametrize("W,T,H", [(1, 4096, 2048), (1, 8192, 1024), (1, 16384, 512), (1, 4097, 1536),
+                                   (1, 2049, 2048), (2, 8191, 1024), (2, 4096, 2048), (2, 8192, 512),
+                                   (2, 2047, 1536)])
+def test_few_ranks_short_rows(W, T, H):
+    plan, _ = parity(W, T, H, seed=T + H + W)
     assert plan["variant"] == ROW and plan["vec_per_thread"] == 4 and plan["threads_per_row"] <= 64
 
 
