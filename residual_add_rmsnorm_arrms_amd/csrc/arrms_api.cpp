@@ -45,7 +45,7 @@ constexpr long kXcdRunBytes = 3L << 20;
 // 5.6 TB/s at W=4 against 5.1 TB/s with four vectors per lane).
 constexpr int kReduceAutoVpt = 1;
 // Rows with less traffic than this never use split-H automatically.
-constexpr long kSplitMinRowBytes = 96L << 10;
+constexpr long kSplitMinRowBytes = 144L << 10;
 
 int chunks_capacity(int max_hidden) {
     const int nvec = (max_hidden + 7) / 8;
@@ -240,15 +240,19 @@ void plan_scalar(int tokens, int hidden, arrms_plan_t* p) {
     p->xcd_chunk = 0;
 }
 
-// Automatic crossover to split-H, measured on MI355X with HIP-graph replay
-// (GPU time per call): rows of up to 28 KiB of traffic (W=4 H=2048) are
-// faster with the one-kernel row variant at every T; rows of 110-224 KiB
-// (W=8 H=5120 / H=8192, W=4 H=16384) are faster split over several
-// workgroups while T stays below about 64 rows per 96 KiB of row traffic.
+// Automatic crossover to split-H, measured on MI355X with HIP-graph replay (GPU
+// time per call) on ten shapes with 110-350 KiB of traffic per row: below about
+// 144 KiB per row (W=4 H=8192, W=8 H=5120 and 6144, W=2 H=12288) split-H at best
+// ties the one-kernel row variant at T=1 and loses 10-20 % from T=8 on; above it,
+// split-H wins while T stays below a crossover that grows with the row, from about
+// 64 rows at 160 KiB to about 100 at 176-224 KiB and 128-192 at 350 KiB.  So: T up
+// to cu/4 rows per 32 KiB of row traffic beyond 128 KiB, at most cu/2 rows.
 int auto_splith_max_tokens(int cu_count, int world, int hidden) {
     const long row_bytes = 2L * (world + 3) * hidden;
     if (row_bytes < kSplitMinRowBytes) return 0;
-    return static_cast<int>((cu_count / 4) * row_bytes / kSplitMinRowBytes);
+    long t = (cu_count / 4) * (row_bytes - (128L << 10)) / (32L << 10);
+    if (t > cu_count / 2) t = cu_count / 2;
+    return static_cast<int>(t);
 }
 
 }  // namespace
