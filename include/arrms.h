@@ -93,6 +93,11 @@ typedef struct {
 
 /*
  * Create a handle bound to HIP device `device`.
+ * Source: page 1, section Implementation 4 ("Host-side NVSHMEM lifecycle"),
+ * which gives the operator's host side an initialization step, symmetric
+ * workspace management and a host-side C ABI.  On one GPU that is: bind the
+ * device, read its compute-unit count and allocate the workspace, all once,
+ * here, so that arrms_fused never allocates.
  *   max_world  : largest W a call will pass, 1..ARRMS_MAX_WORLD
  *   max_tokens : largest T a call will pass, >= 0
  *   max_hidden : largest H a call will pass, 1..ARRMS_MAX_HIDDEN
@@ -108,6 +113,9 @@ int arrms_create(arrms_handle_t* out, int device, int max_world, int max_tokens,
 
 /*
  * Enqueue the fused operator on `stream` (0 = the null stream of the handle's device).
+ * Source: page 1, section Summary (the three-line contract above) and section
+ * Implementation 3 (the residual + RMSNorm epilogue after the reduction); rows
+ * map to workgroups as in section Implementation 2 (Row-parallel execution).
  *   partials     : HOST array of `world` device pointers, each BF16 [tokens][hidden];
  *                  read at call time, the caller may free the array on return
  *   world        : W, 1..max_world
@@ -133,12 +141,15 @@ int arrms_fused(arrms_handle_t h, const void* const* partials, int world, int to
 
 /*
  * Free the handle's workspace and the handle.  NULL is accepted (ARRMS_OK).
+ * Source: page 1, section Implementation 4 ("Host-side NVSHMEM lifecycle"),
+ * its resource-cleanup step.
  * The caller must make sure no call on the handle is still executing
  * (synchronise its stream first).  Using a destroyed handle is undefined.
  */
 int arrms_destroy(arrms_handle_t h);
 
-/* Static text for a status code ("unknown status" for others). */
+/* Static text for a status code ("unknown status" for others).  Part of the
+ * host-side C ABI of page 1, section Implementation 4. */
 const char* arrms_status_string(int status);
 
 /* hipError_t of the last failed HIP call on this handle (0 if none; -1 for a NULL handle).

@@ -5,7 +5,7 @@
 // The page "[TLERaw] Add NVSHMEM allreduce RMSNorm tutorial" (FlagTree PR #1122),
 // section Implementation 4, gives its host side an init / workspace / cleanup
 // life cycle behind a C ABI; here the one-time work (device query, workspace
-// allocation and zeroing, reading the variant override) happens in
+// allocation, reading the variant override) happens in
 // arrms_create only, and arrms_fused does no allocation and no synchronisation.
 #include "arrms.h"
 
@@ -140,7 +140,9 @@ int plan_row(int cu_count, int world, int tokens, int hidden, const arrms_tuning
     // partial round made them up to 12 % slower.  Three ranks won at some of these
     // shapes and lost up to 4 % at others, and W >= 4 loses (8 % at W=4 H=2048
     // T=4096), so they keep one vector per lane.
-    const bool layout_tuned = t && (t->vec_per_thread || t->threads_per_row);
+    // A tuned lane layout or row count per workgroup is taken as given: the
+    // four-vector layout is an automatic choice only.
+    const bool layout_tuned = t && (t->vec_per_thread || t->threads_per_row || t->rows_per_block);
     if (!layout_tuned && world <= 2 && nvec >= 64 && nvec <= 256) {
         const int tpr4 = pow2_threads((nvec + 3) / 4);
         const long blocks4 = (static_cast<long>(tokens) + 256 / tpr4 - 1) / (256 / tpr4);
@@ -244,9 +246,12 @@ void plan_scalar(int tokens, int hidden, arrms_plan_t* p) {
 // time per call) on ten shapes with 110-350 KiB of traffic per row: below about
 // 144 KiB per row (W=4 H=8192, W=8 H=5120 and 6144, W=2 H=12288) split-H at best
 // ties the one-kernel row variant at T=1 and loses 10-20 % from T=8 on; above it,
-// split-H wins while T stays below a crossover that grows with the row, from about
-// 64 rows at 160 KiB to about 100 at 176-224 KiB and 128-192 at 350 KiB.  So: T up
-// to cu/4 rows per 32 KiB of row traffic beyond 128 KiB, at most cu/2 rows.
+// split-H wins while T stays below a crossover that grows with the row (about 64
+// rows at 160 KiB, about 100 at 176-224 KiB, between 128 and 192 at 350 KiB).
+// Rule: split while T <= (cu/4) * (row KiB - 128) / 32, capped at cu/2.  With 256
+// CUs that is 64 rows at 160 KiB, 96 at 176 KiB and the cap of 128 from 192 KiB
+// up; the cap stays below the measured crossover of the longest rows, where the
+// row kernel is the safe side.  Rows under 144 KiB never split automatically.
 int auto_splith_max_tokens(int cu_count, int world, int hidden) {
     const long row_bytes = 2L * (world + 3) * hidden;
     if (row_bytes < kSplitMinRowBytes) return 0;
@@ -342,12 +347,14 @@ int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
     }
     int split_max = (tuning && tuning->splith_max_tokens >= 0) ? tuning->splith_max_tokens
                                                               : auto_splith_max_tokens(cu_count, world, hidden);
+    // The automatic choice always finds a plan: tuning overrides that no vector
+    // kernel can honour end in the element-wise kernel (same results).
     if (hidden > ARRMS_ROW_MAX_HIDDEN || tokens <= split_max) {
-        const int rc = plan_splith(cu_count, max_hidden, world, tokens, hidden, tuning, plan);
-        if (rc == ARRMS_OK || hidden > ARRMS_ROW_MAX_HIDDEN) return rc;
+        if (plan_splith(cu_count, max_hidden, world, tokens, hidden, tuning, plan) == ARRMS_OK) return ARRMS_OK;
         memset(plan, 0, sizeof *plan);
     }
-    if (plan_row(cu_count, world, tokens, hidden, tuning, plan) == ARRMS_OK) return ARRMS_OK;
+    if (hidden <= ARRMS_ROW_MAX_HIDDEN && plan_row(cu_count, world, tokens, hidden, tuning, plan) == ARRMS_OK)
+        return ARRMS_OK;
     // A row the row kernels cannot hold in registers: split it, else go element-wise.
     memset(plan, 0, sizeof *plan);
     if (plan_splith(cu_count, max_hidden, world, tokens, hidden, tuning, plan) == ARRMS_OK) return ARRMS_OK;

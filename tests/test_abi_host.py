@@ -36,6 +36,24 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def declaration_comment(name):
+    """The comment block directly above the declaration of `name` in the header."""
+    text = open(HEADER).read()
+    m = re.search(r"(/\*(?:(?!\*/).)*\*/)\s*(?:int|const char\*)\s+%s\s*\(" % name, text, re.S)
+    assert m, name
+    return m.group(1)
+
+
+@pytest.mark.parametrize("name", ["arrms_create", "arrms_fused", "arrms_destroy", "arrms_status_string",
+                                  "arrms_reduce"])
+def test_boundary_exports_cite_a_section_of_the_page(name):
+    """Each entry point of the boundary names the passage of the page that defines it."""
+    c = declaration_comment(name)
+    assert re.search(r"section (Summary|Implementation \d)", c), name
+    # the comment belongs to this declaration only (no other declaration in between)
+    assert not re.search(r"^\s*(int|const char\*)\s+arrms_\w+\s*\(", c, re.M)
+
+
 def test_status_strings():
     assert A.arrms_status_string(A.ARRMS_OK) == "ok"
     assert A.arrms_status_string(A.ARRMS_ERR_INVALID_ARG) == "invalid argument"
@@ -320,6 +338,46 @@ def test_rows_per_block_tuning():
     assert rc == A.ARRMS_OK and p["rows_per_block"] == 4 and p["block"] == 1024 and p["blocks"] == 1024
     rc, p = plan(4, 4096, 2048, variant=A.ARRMS_VARIANT_ROW, tuning=A.arrms_tuning_t.make(rows_per_block=8))
     assert rc == A.ARRMS_ERR_UNSUPPORTED                      # 2048 threads per workgroup
+
+
+def test_tuned_rows_per_block_keeps_one_vector_layout():
+    """Tuning only the rows per workgroup is a layout override: the automatic four-vector
+    layout (16 lanes per row at H=512) is not taken, so the row kernel still runs."""
+    rc, p = plan(1, 16384, 512, tuning=A.arrms_tuning_t.make(rows_per_block=1))
+    assert rc == A.ARRMS_OK
+    assert (p["variant"], p["vec_per_thread"], p["threads_per_row"], p["rows_per_block"]) == (
+        A.ARRMS_VARIANT_ROW, 1, 64, 1)
+
+
+@pytest.mark.parametrize("tuning", [dict(vec_per_thread=4), dict(vec_per_thread=8), dict(splith_block=64)])
+def test_automatic_choice_never_fails_under_tuning(tuning):
+    """Tuning changes speed only: where no vector kernel can honour it, the automatic
+    choice ends in the element-wise kernel instead of refusing the call."""
+    for W, T, H in ((4, 3, 32768), (4, 5000, 65536), (8, 2, 8192), (4, 4096, 2048)):
+        rc, p = plan(W, T, H, tuning=A.arrms_tuning_t.make(**tuning))
+        assert rc == A.ARRMS_OK, (W, T, H, tuning)
+        assert p["variant"] in (A.ARRMS_VARIANT_ROW, A.ARRMS_VARIANT_SPLITH, A.ARRMS_VARIANT_SCALAR)
+        assert p["grid"] > 0
+
+
+@pytest.mark.parametrize("W,T,H,variant", [
+    (8, 1, 5120, A.ARRMS_VARIANT_ROW),          # 110 KiB per row: below 144 KiB, never split
+    (4, 1, 8192, A.ARRMS_VARIANT_ROW),          # 112 KiB
+    (2, 1, 12288, A.ARRMS_VARIANT_ROW),         # 120 KiB
+    (8, 1, 6144, A.ARRMS_VARIANT_ROW),          # 132 KiB
+    (8, 96, 8192, A.ARRMS_VARIANT_SPLITH),      # 176 KiB: split up to 64 * 48 / 32 = 96 rows
+    (8, 97, 8192, A.ARRMS_VARIANT_ROW),
+    (4, 128, 16384, A.ARRMS_VARIANT_SPLITH),    # 224 KiB: 192 by the slope, capped at 128
+    (4, 129, 16384, A.ARRMS_VARIANT_ROW),
+    (16, 48, 4096, A.ARRMS_VARIANT_SPLITH),     # 152 KiB: 64 * 24 / 32 = 48 rows
+    (16, 49, 4096, A.ARRMS_VARIANT_ROW),
+    (16, 129, 6144, A.ARRMS_VARIANT_SPLITH),    # the row kernels cannot hold this row at W=16
+])
+def test_splith_crossover_boundaries(W, T, H, variant):
+    """The automatic split-H rule with 256 CUs: rows of 144 KiB or more split while
+    T <= 64 * (row KiB - 128) / 32, at most 128 rows."""
+    rc, p = plan(W, T, H)
+    assert rc == A.ARRMS_OK and p["variant"] == variant, (W, T, H, p)
 
 
 def test_binding_fails_loudly_without_the_library(tmp_path):
