@@ -16,7 +16,17 @@ T = 4096, 8192, 16384 (beyond the metric's range) separate the per-call fixed ti
 from the kernel's streaming rate.
 
 `--workload large_hidden` (W=8 T=8192 H=8192) or `--workload ragged_outliers`
-(W=8 T=16383 H=5120, 1% outliers) times those shapes instead, headline only.
+(W=8 T=16383 H=5120, 1% outliers) times those shapes instead, headline only.  Any
+shape can be timed the same way (rotating pool, oracle parity check, CPU baseline,
+JSON) with `--world/--tokens/--hidden/--eps/--x-sigma/--outlier-p/--seed`, which
+replace the named workload's values (the page's harness, section Implementation 6,
+likewise takes configurable token shapes).
+
+Timing: `value`/`ms_per_step` are host wall clock over the K timed calls between two
+synchronisations; `roofline` uses HIP events on the launch stream over the same calls.
+The `ceiling` section times the library's most read-heavy kernel (the rank sum alone,
+W=8 and W=16) on the same pool as what this GPU streams, and reports the fused
+headline as a fraction of it.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -42,9 +52,10 @@ SWEEP_T = [1, 16, 64, 128, 256, 1024, 4096]
 FIT_T = [4096, 8192, 16384]
 POOL_ROWS = 16384
 POOL_SLOTS = 10
-# the fused kernels and the device helpers they include
+# what decides the headline launch: the fused kernels and their device helpers, the
+# host planner that picks variant, lane layout and XCD runs, and the argument packing
 KERNEL_SRC = [os.path.join(ROOT, "residual_add_rmsnorm_arrms_amd", "csrc", f)
-              for f in ("arrms_device.h", "arrms_kernels.hip")]
+              for f in ("arrms_device.h", "arrms_kernels.hip", "arrms_api.cpp", "arrms_internal.h")]
 # workloads the benchmark can time (--workload); the default is the metric's own
 BENCH_WORKLOADS = ("prefill", "large_hidden", "ragged_outliers")
 
@@ -58,8 +69,9 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    """Hash of the kernel source without comments and blank lines: what the counters were
-    measured on (a comment edit leaves it unchanged, a code edit does not)."""
+    """Hash of the kernel, planner and argument-packing source without comments and blank
+    lines: what the counters were measured on (a comment edit leaves it unchanged, a code
+    edit does not)."""
     import re
     text = "".join(open(f).read() for f in KERNEL_SRC)
     text = re.sub(r"//[^\n]*", "", text)
@@ -71,11 +83,21 @@ def algorithmic_bytes(W, T, H):
     return 2 * T * H * (W + 3) + 2 * H
 
 
+def pool_slots(torch, slot_bytes):
+    """Slots of a rotating pool: POOL_SLOTS when they fit in half the GPU's memory, else as
+    many as fit (at least 2, so that consecutive calls never share buffers)."""
+    total = torch.cuda.get_device_properties(0).total_memory
+    n = min(POOL_SLOTS, int(0.5 * total // slot_bytes))
+    if n < 2:
+        raise SystemExit("bench.py: two pool slots of %.1f GiB do not fit this GPU" % (slot_bytes / 2 ** 30))
+    return n
+
+
 class Pool:
-    """POOL_SLOTS slots, each holding W partials, residual, residual_out and norm_out of
-    [rows, H] BF16 in one device allocation (the input rows repeated to fill `rows`).
-    A call with T rows uses rows [j*T, (j+1)*T) of one slot, so successive calls touch
-    fresh memory."""
+    """Slots (POOL_SLOTS, fewer for very large shapes), each holding W partials, residual,
+    residual_out and norm_out of [rows, H] BF16 in one device allocation (the input rows
+    repeated to fill `rows`).  A call with T rows uses rows [j*T, (j+1)*T) of one slot, so
+    successive calls touch fresh memory."""
 
     def __init__(self, torch, x, res, w, rows=None):
         W, T_in, H = x.shape
@@ -83,14 +105,15 @@ class Pool:
         self.W, self.T, self.H = W, T, H
         dev = torch.device("cuda", 0)
         self.tensor_elems = T * H
-        self.slot = torch.empty((POOL_SLOTS, W + 3, T, H), dtype=torch.bfloat16, device=dev)
+        self.slots = pool_slots(torch, (W + 3) * T * H * 2)
+        self.slot = torch.empty((self.slots, W + 3, T, H), dtype=torch.bfloat16, device=dev)
         xd, rd = x.to(dev), res.to(dev)
         for r0 in range(0, T, T_in):
             n = min(T_in, T - r0)
             self.slot[0, :W, r0:r0 + n].copy_(xd[:, :n])
             self.slot[0, W, r0:r0 + n].copy_(rd[:n])
         del xd, rd
-        for s in range(1, POOL_SLOTS):
+        for s in range(1, self.slots):
             self.slot[s, :W + 1].copy_(self.slot[0, :W + 1])
         self.weight = w.to(dev)
         torch.cuda.synchronize()
@@ -101,16 +124,16 @@ class Pool:
         return self.slot.numel() * 2
 
     def reduced_ptr(self, base, T, j, s):
-        """Address of the reduced-output rows of set (j, s) in a [POOL_SLOTS, rows, H] buffer."""
+        """Address of the reduced-output rows of set (j, s) in a [slots, rows, H] buffer."""
         return base + s * self.tensor_elems * 2 + j * T * self.H * 2
 
     def sets(self, T, max_sets=8192):
         """Pointer sets (partials, residual, residual_out, norm_out) for T-row calls: up to
         max_sets distinct ones, cycling through the slots first."""
-        per_slot = min(self.T // T, max(1, max_sets // POOL_SLOTS))
+        per_slot = min(self.T // T, max(1, max_sets // self.slots))
         out = []
         for j in range(per_slot):
-            for s in range(POOL_SLOTS):
+            for s in range(self.slots):
                 slot = self.base + s * (self.W + 3) * self.tensor_elems * 2
                 off = j * T * self.H * 2
                 t = lambda k: slot + k * self.tensor_elems * 2 + off
@@ -126,15 +149,15 @@ class ReduceCaller:
         lib = A.load()
         self.fn = lib.arrms_reduce
         vp = ctypes.c_void_p
-        per_slot = min(pool.T // T, max(1, 8192 // POOL_SLOTS))
+        per_slot = min(pool.T // T, max(1, 8192 // pool.slots))
         inputs_per_slot = pool.W + 1
         self.args = []
         te = pool.tensor_elems * 2
         for j in range(per_slot):
-            for s in range(POOL_SLOTS):
+            for s in range(pool.slots):
                 parts = []
                 for r in range(W):
-                    slot = (s + r // inputs_per_slot) % POOL_SLOTS
+                    slot = (s + r // inputs_per_slot) % pool.slots
                     parts.append(pool.base + slot * (pool.W + 3) * te + (r % inputs_per_slot) * te + j * T * pool.H * 2)
                 out = pool.reduced_ptr(out_base, T, j, s)
                 self.args.append((vp(handle), (vp * W)(*parts), W, T, pool.H, vp(out)))
@@ -377,14 +400,15 @@ def cpu_baseline(x, res, w, eps, budget_s):
     }
 
 
-def traffic_record(wl):
-    """FETCH_SIZE / WRITE_SIZE per launch measured by rocprofv3 for the current kernel source
-    on workload wl, or None when the counters were taken on another version of the kernels."""
+def traffic_record(wl, plan):
+    """DRAM bytes per launch measured by rocprofv3 for workload wl, or None unless they were
+    taken on the current kernel, planner and argument-packing source and on the same launch
+    plan as this run's."""
     path = traffic_file(wl)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash() or rec.get("plan") != plan:
         return None
     return rec
 
@@ -422,6 +446,13 @@ def sweep_tokens(ctx):
         d = time_per_launch(torch, c, 300)
         iso = time_isolated(torch, c, 100)
         gr = time_graph(torch, c, 100, 10)
+        # the same call repeated on one set of buffers (inputs and outputs stay in the caches)
+        hot = Caller(ctx.A, ctx.op.handle, ctx.pool.sets(t)[:1], W, t, H, ctx.pool.weight.data_ptr(), ctx.eps,
+                     ctx.stream)
+        for _ in range(100):
+            hot()
+        _, gpu_hot = time_back_to_back(torch, hot, k)
+        gr_hot = time_graph(torch, hot, 100, 10)
         b = algorithmic_bytes(W, t, H)
         row = {"T": t, "variant": VARIANT_NAMES[p["variant"]], "grid": p["grid"],
                "block": p["block"], "bytes": b,
@@ -429,14 +460,16 @@ def sweep_tokens(ctx):
                "us_event_pair_p50": pct(d, 50) * 1e3, "us_event_pair_p90": pct(d, 90) * 1e3,
                "us_event_pair_p99": pct(d, 99) * 1e3,
                "us_isolated_p50": pct(iso, 50) * 1e3, "us_graph_replay": gr * 1e3,
+               "us_back_to_back_gpu_hot": gpu_hot * 1e3, "us_graph_replay_hot": gr_hot * 1e3,
                "GB_s_back_to_back": b / (gpu * 1e-3) / 1e9,
                "GB_s_graph": b / (gr * 1e-3) / 1e9}
         row["frac_peak_back_to_back"] = row["GB_s_back_to_back"] / HBM_PEAK_GBS
         sweep.append(row)
         log("T=%5d %-6s b2b %.2f us (%.0f GB/s, %.1f%%), event pair p50 %.2f us, isolated %.2f us, "
-            "graph %.2f us" % (t, row["variant"], row["us_back_to_back_gpu"], row["GB_s_back_to_back"],
-                               100 * row["frac_peak_back_to_back"], row["us_event_pair_p50"],
-                               row["us_isolated_p50"], row["us_graph_replay"]))
+            "graph %.2f us; one hot set: b2b %.2f us, graph %.2f us" % (
+                t, row["variant"], row["us_back_to_back_gpu"], row["GB_s_back_to_back"],
+                100 * row["frac_peak_back_to_back"], row["us_event_pair_p50"], row["us_isolated_p50"],
+                row["us_graph_replay"], row["us_back_to_back_gpu_hot"], row["us_graph_replay_hot"]))
     return sweep
 
 
@@ -469,12 +502,12 @@ def fusion_and_rank_sum(ctx, T, nbytes, fused_ms):
     call through a BF16 `reduced` tensor) against the fused call; then the rank sum
     alone over sizes and W (reads W partials, writes reduced)."""
     torch, A, op, pool, W, H = ctx.torch, ctx.A, ctx.op, ctx.pool, ctx.W, ctx.H
-    red_pool = torch.empty((POOL_SLOTS, pool.T, H), dtype=torch.bfloat16, device="cuda")
+    red_pool = torch.empty((pool.slots, pool.T, H), dtype=torch.bfloat16, device="cuda")
     rcall = ReduceCaller(A, op.handle, pool, W, T, red_pool.data_ptr(), ctx.stream)
-    per_slot = len(pool.sets(T)) // POOL_SLOTS
-    epi_sets = [([pool.reduced_ptr(red_pool.data_ptr(), T, i // POOL_SLOTS, i % POOL_SLOTS)], st[1], st[2], st[3])
+    per_slot = len(pool.sets(T)) // pool.slots
+    epi_sets = [([pool.reduced_ptr(red_pool.data_ptr(), T, i // pool.slots, i % pool.slots)], st[1], st[2], st[3])
                 for i, st in enumerate(pool.sets(T))]
-    assert len(epi_sets) == per_slot * POOL_SLOTS
+    assert len(epi_sets) == per_slot * pool.slots
     ecall = Caller(A, op.handle, epi_sets, 1, T, H, pool.weight.data_ptr(), ctx.eps, ctx.stream)
 
     def two_stage():
@@ -550,14 +583,61 @@ def world_sweep(ctx, T=4096, worlds=(1, 2, 3, 4, 6, 8, 12, 16)):
         _, g = time_back_to_back(torch, c, 500)
         b = algorithmic_bytes(W, T, H)
         out.append({"W": W, "T": T, "H": H, "us": g * 1e3, "GB_s": b / (g * 1e-3) / 1e9,
-                    "frac_of_peak": b / (g * 1e-3) / 1e9 / HBM_PEAK_GBS, "vec_per_thread": p["vec_per_thread"],
+                    "frac_of_peak_gpu_events": b / (g * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "vec_per_thread": p["vec_per_thread"],
                     "threads_per_row": p["threads_per_row"], "xcd_chunk": p["xcd_chunk"]})
         log("W=%2d T=%d H=%d: %.2f us, %.0f GB/s (%.1f%%)" % (W, T, H, g * 1e3, b / (g * 1e-3) / 1e9,
-                                                           100 * out[-1]["frac_of_peak"]))
+                                                           100 * out[-1]["frac_of_peak_gpu_events"]))
         wop.close()
         del wpool
         torch.cuda.empty_cache()
     return out
+
+
+def read_ceiling(ctx, achieved_gbs, T=16384, worlds=(8, 16)):
+    """What this GPU streams with the library's own most read-heavy kernel: the rank sum
+    alone (arrms_reduce, W reads per write) at T=16384 H=2048, back-to-back GPU time.
+    Each call reads W distinct 64 MiB input tensors of the prefill pool (its 10 slots hold
+    50), consecutive calls take disjoint ones, and outputs rotate over 10 buffers, so no
+    call finds its inputs in the 256 MB Infinity Cache.  The fused headline's achieved
+    bandwidth is reported as a fraction of the faster of these rates."""
+    torch, A, op, pool, H = ctx.torch, ctx.A, ctx.op, ctx.pool, ctx.H
+    assert pool.T >= T
+    fn = A.load().arrms_reduce
+    vp = ctypes.c_void_p
+    te = pool.tensor_elems * 2
+    inputs = [pool.base + s * (pool.W + 3) * te + k * te for s in range(pool.slots) for k in range(pool.W + 1)]
+    out = torch.empty((pool.slots, T, H), dtype=torch.bfloat16, device="cuda")
+    res = {}
+    for W in worlds:
+        calls = []
+        for i in range(len(inputs)):
+            parts = [inputs[(i * W + r) % len(inputs)] for r in range(W)]
+            calls.append((vp(op.handle), (vp * W)(*parts), W, T, H, vp(out[i % pool.slots].data_ptr()),
+                          vp(ctx.stream)))
+        state = {"i": 0}
+
+        def call():
+            a = calls[state["i"]]
+            state["i"] = (state["i"] + 1) % len(calls)
+            rc = fn(*a)
+            if rc:
+                raise RuntimeError("arrms_reduce returned %d" % rc)
+        for _ in range(20):
+            call()
+        _, ms = time_back_to_back(torch, call, 200)
+        b = 2 * T * H * (W + 1)
+        res["reduce_W%d" % W] = {"W": W, "T": T, "H": H, "bytes": b, "us": ms * 1e3, "GB_s": b / (ms * 1e-3) / 1e9,
+                                 "frac_of_peak": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        log("ceiling: rank sum alone W=%d T=%d H=%d: %.2f us, %.0f GB/s (%.1f%% of 8 TB/s)" % (
+            W, T, H, ms * 1e3, b / (ms * 1e-3) / 1e9, 100 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS))
+    del out
+    best = max(v["GB_s"] for v in res.values())
+    res["ceiling_GB_s"] = best
+    res["fused_headline_GB_s"] = achieved_gbs
+    res["fused_frac_of_ceiling"] = achieved_gbs / best
+    log("fused headline %.0f GB/s = %.1f%% of that ceiling" % (achieved_gbs, 100 * achieved_gbs / best))
+    return res
 
 
 def splith_crossover(ctx):
@@ -601,17 +681,49 @@ def _short_kernel_name(n: str) -> str:
     return n[:70]
 
 
+# Counter passes (one rocprofv3 --pmc run each; at most four TCC counters per run).
+# DRAM bytes come from the gfx950 counters that count DRAM reads and writes in
+# 32-byte units (a 64-byte request counts 2, a 128-byte read 4).
+PMC_PASSES = {
+    "dram": ["TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum", "TCC_EA0_RDREQ_sum",
+             "TCC_BUBBLE_sum"],
+    "size": ["TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum", "TCC_EA0_WRREQ_64B_sum"],
+    "stall": ["TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum", "TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum", "TCC_BUSY_sum",
+              "TCC_EA0_RDREQ_LEVEL_sum"],
+    "fetch": ["FETCH_SIZE"],
+    "write": ["WRITE_SIZE"],
+}
+
+
+def pmc_command(workload: str, name: str) -> str:
+    flag = "" if workload == "prefill" else " --workload %s" % workload
+    return ("timeout -s KILL 180 rocprofv3 --pmc %s --output-format csv -d gpurun_out/pmc_%s -o %s -- "
+            "python -u bench.py%s --no-cpu --no-sweep --steps 50 --warmup 5"
+            % (" ".join(PMC_PASSES[name]), name, name, flag))
+
+
+def read_counters(path: str) -> dict:
+    """{(kernel, grid size): {counter: [value per dispatch]}} from a rocprofv3 counter CSV."""
+    import collections
+    import csv
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        out[(_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size"]))][r["Counter_Name"]].append(
+            float(r["Counter_Value"]))
+    return out
+
+
 def summarize_profiles(run_dir: str, workload: str, out_dir: str = None) -> None:
     """Write profiles/row_kernel_<workload>.md and profiles/traffic_<workload>.json from
-    the outputs of the three rocprofv3 runs named in them (kernel trace of the
-    benchmark command; FETCH_SIZE and WRITE_SIZE passes), found under run_dir
-    (bench.json, prof_bench/, pmc_fetch/, pmc_write/)."""
+    the rocprofv3 outputs found under run_dir: bench.json and prof_bench/ (kernel trace of
+    the benchmark command), pmc_<pass>/ for the counter passes of PMC_PASSES."""
     import collections
     import csv
     import synth
     wl = synth.WORKLOADS[workload]
     W, T, H = wl.world, wl.tokens, wl.hidden
     alg = algorithmic_bytes(W, T, H)
+    alg_read, alg_write = 2 * T * H * (W + 1) + 2 * H, 2 * T * H * 2
     sha = kernel_source_hash()
     bench = json.load(open(os.path.join(run_dir, "bench.json")))
     plan = bench["config"]["plan"]
@@ -625,55 +737,61 @@ def summarize_profiles(run_dir: str, workload: str, out_dir: str = None) -> None
     kname = max((len(v), k) for k, v in trace.items()
                 if k[1] == grid_threads and k[2] == plan["block"] and "kernel<" in k[0])[1][0]
     head = trace[(kname, grid_threads, plan["block"])]
-
-    def counter(path):
-        out = collections.defaultdict(list)
-        for r in csv.DictReader(open(path)):
-            out[(_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
-        return out
-    fetch = counter(os.path.join(run_dir, "pmc_fetch", "fetch_counter_collection.csv"))
-    write = counter(os.path.join(run_dir, "pmc_write", "write_counter_collection.csv"))
     kkey = (kname, grid_threads)
-    f_raw, w_raw = statistics.mean(fetch[kkey]), statistics.mean(write[kkey])
-    # calibration: the 512 MiB device copy of copy_context (its WRITE_SIZE is 512 MiB)
-    copy_bytes = 512 * 2 ** 20
-    cw = max(v for (k, _), vs in write.items() if "copyBuffer" in k for v in vs
-             if abs(v * 1024 - copy_bytes) < 0.02 * copy_bytes)
-    cf = min((v for (k, _), vs in fetch.items() if "copyBuffer" in k for v in vs),
-             key=lambda v: abs(v * 1024 * 2 - copy_bytes))
-    fscale, wscale = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
-    fb, wb = f_raw * 1024 * fscale, w_raw * 1024 * wscale
-    cmd_trace = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
-                 "-d gpurun_out/prof_bench -o bench -- python -u bench.py" + flag)
-    cmd_f = ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- "
-             "python -u bench.py%s --no-cpu %s--steps 50 --warmup 5" % (flag, "--no-sweep " if workload == "prefill" else ""))
-    cmd_w = cmd_f.replace("FETCH_SIZE", "WRITE_SIZE").replace("pmc_fetch", "pmc_write").replace("-o fetch", "-o write")
+    mean = {}
+    dispatches = {}
+    for name in PMC_PASSES:
+        path = os.path.join(run_dir, "pmc_%s" % name, "%s_counter_collection.csv" % name)
+        if not os.path.exists(path):
+            continue
+        c = read_counters(path)[kkey]
+        for cn, vals in c.items():
+            mean[cn] = statistics.mean(vals)
+            dispatches[cn] = len(vals)
+    rd = 32 * mean["TCC_EA0_RDREQ_DRAM_32B_sum"]
+    wr = 32 * mean["TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"]
+    by_size = None
+    if "TCC_EA0_RDREQ_128B_sum" in mean:
+        by_size = (32 * mean["TCC_EA0_RDREQ_32B_sum"] + 64 * mean["TCC_EA0_RDREQ_64B_sum"] +
+                   128 * mean["TCC_EA0_RDREQ_128B_sum"])
+    # the derived FETCH_SIZE's own formula on gfx950, from its raw terms
+    fetch_formula = (128 * mean["TCC_BUBBLE_sum"] + 64 * (mean["TCC_EA0_RDREQ_sum"] - mean["TCC_BUBBLE_sum"] -
+                                                          mean.get("TCC_EA0_RDREQ_32B_sum", 0.0)) +
+                     32 * mean.get("TCC_EA0_RDREQ_32B_sum", 0.0))
+    stalls = None
+    if "TCC_BUSY_sum" in mean:
+        busy = mean["TCC_BUSY_sum"]
+        stalls = {"tcc_busy_cycles_sum": busy,
+                  "read_dram_credit_stall_pct_of_busy": 100 * mean["TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum"] / busy,
+                  "write_dram_credit_stall_pct_of_busy": 100 * mean["TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum"] / busy,
+                  "mean_read_requests_in_flight_per_busy_cycle": mean["TCC_EA0_RDREQ_LEVEL_sum"] / busy,
+                  "mean_read_latency_cycles": mean["TCC_EA0_RDREQ_LEVEL_sum"] / mean["TCC_EA0_RDREQ_sum"]}
+    commands = [pmc_command(workload, n) for n in PMC_PASSES]
     base = "%s_w%d_h%d_t%d" % (workload, W, H, T)
     traffic = {
         "kernel": kname, "workload": "W=%d T=%d H=%d (%s), launch grid %d x %d" % (W, T, H, workload, plan["grid"],
                                                                                 plan["block"]),
-        "dispatches": len(fetch[kkey]),
-        "fetch_kib_per_dispatch_raw": f_raw, "write_kib_per_dispatch_raw": w_raw,
-        "copy_calibration": {"kernel": "__amd_rocclr_copyBuffer (torch copy_ of 512 MiB bf16)",
-                             "bytes_read": copy_bytes, "bytes_written": copy_bytes, "fetch_kib_raw": cf,
-                             "write_kib_raw": cw, "fetch_scale": fscale, "write_scale": wscale},
-        "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
-        "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": (fb + wb) / alg,
-        "kernel_source_sha256_16": sha, "commands": [cmd_f, cmd_w],
+        "plan": plan, "dispatches": dispatches, "counters_mean_per_dispatch": mean,
+        "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+        "algorithmic_read_bytes": alg_read, "algorithmic_write_bytes": alg_write,
+        "read_bytes_by_request_size": by_size, "fetch_size_formula_bytes": fetch_formula,
+        "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": (rd + wr) / alg,
+        "stalls": stalls, "kernel_source_sha256_16": sha, "commands": commands,
     }
     out_dir = out_dir or os.path.join(ROOT, "profiles")
     json.dump(traffic, open(os.path.join(out_dir, os.path.basename(traffic_file(wl))), "w"), indent=1)
+    cmd_trace = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
+                 "-d gpurun_out/prof_bench -o bench -- python -u bench.py" + flag)
     L = ["# %s on W=%d T=%d H=%d (%s) — rocprofv3 summary\n" % (kname, W, T, H, workload),
-         "GPU: MI355X (gfx950), one GPU.  Kernel source hash (sha256[:16] of the code without comments, as "
-         "bench.py computes it) = `%s`.  Written by `python bench.py --summarize <run dir>%s` from the runs below.\n"
-         % (sha, flag),
+         "GPU: MI355X (gfx950), one GPU.  Source hash of the kernels, planner and argument packing (sha256[:16] "
+         "of the code without comments, as bench.py computes it) = `%s`.  Written by `python bench.py --summarize "
+         "<run dir>%s` from the runs below.\n" % (sha, flag),
          "## Kernel trace (same command as the benchmark)\n", "```\n%s\n```\n" % cmd_trace]
     if workload == "prefill":
-        L.append("Dispatches grouped by kernel and launch shape (grid in threads). Every T of the sweep uses "
-                 "`row_kernel<4, 1>` (the headline launch is grid %d x %d threads); the split-H and scalar kernels "
-                 "come from the forced-variant and split-H sections, `reduce_kernel` from the rank-sum sections, "
-                 "`copyBuffer` from the copy references. Shapes with fewer than 3 dispatches are left out.\n"
-                 % (plan["grid"], plan["block"]))
+        L.append("Dispatches grouped by kernel and launch shape (grid in threads). The headline launch is `%s`, grid "
+                 "%d x %d threads; other launch shapes come from the token sweep, the forced-variant, split-H, "
+                 "rank-sum and ceiling sections and the copy references. Shapes with fewer than 3 dispatches are "
+                 "left out.\n" % (kname, plan["grid"], plan["block"]))
     else:
         L.append("Dispatches grouped by kernel and launch shape (grid in threads); the headline launch is `%s`, grid "
                  "%d x %d threads, and `copyBuffer` comes from the copy references. Shapes with fewer than 3 "
@@ -690,18 +808,52 @@ def summarize_profiles(run_dir: str, workload: str, out_dir: str = None) -> None
              "bench.py reported %.2f us per launch from HIP events over its timed region (%.1f GB/s).\n" % (
                  hm, len(head), alg / (hm * 1e-6) / 1e9, alg, bench["roofline"]["kernel_mean_us"],
                  bench["roofline"]["achieved"]))
-    L += ["## HBM traffic (FETCH_SIZE, WRITE_SIZE), one counter per run\n", "```\n%s\n%s\n```\n" % (cmd_f, cmd_w),
-          "Calibration: the 512 MiB device copy in the same runs (`__amd_rocclr_copyBuffer`) reads FETCH_SIZE = "
-          "%.1f KiB and WRITE_SIZE = %.1f KiB per dispatch for 524288 KiB read and written, so FETCH_SIZE is "
-          "scaled by %.4f and WRITE_SIZE by %.4f.\n" % (cf, cw, fscale, wscale),
-          "| counter | raw KiB / dispatch | scaled bytes / launch | algorithmic bytes |", "|---|---|---|---|",
-          "| FETCH_SIZE | %.1f | %.0f | %d (read: W partials + residual + weight) |" % (
-              f_raw, fb, 2 * T * H * (W + 1) + 2 * H),
-          "| WRITE_SIZE | %.1f | %.0f | %d (residual_out + norm_out) |" % (w_raw, wb, 2 * T * H * 2),
-          "\nTotal traffic / algorithmic bytes = %.4f over %d dispatches.\n" % ((fb + wb) / alg, len(fetch[kkey]))]
+    L += ["## HBM traffic from raw TCC counters, one pass per run\n",
+          "```\n%s\n```\n" % "\n".join(commands),
+          "DRAM bytes are 32 x `TCC_EA0_RDREQ_DRAM_32B_sum` (reads) and 32 x `TCC_EA0_WRREQ_WRITE_DRAM_32B_sum` "
+          "(writes): these gfx950 counters count DRAM traffic in 32-byte units, so no calibration factor is "
+          "applied.\n",
+          "| quantity | per launch | algorithmic |", "|---|---|---|",
+          "| DRAM read bytes | %.0f | %d (W partials + residual + weight) |" % (rd, alg_read),
+          "| DRAM write bytes | %.0f | %d (residual_out + norm_out) |" % (wr, alg_write),
+          "| total / algorithmic | %.4f | 1 |" % ((rd + wr) / alg)]
+    if by_size is not None:
+        L += ["| read bytes from request sizes (32 x n32 + 64 x n64 + 128 x n128) | %.0f | |" % by_size,
+              "| read requests of 32 / 64 / 128 bytes | %.0f / %.0f / %.0f | |" % (
+                  mean["TCC_EA0_RDREQ_32B_sum"], mean["TCC_EA0_RDREQ_64B_sum"], mean["TCC_EA0_RDREQ_128B_sum"])]
+    L += ["| `TCC_EA0_RDREQ_sum` / `TCC_BUBBLE_sum` | %.0f / %.0f | |" % (mean["TCC_EA0_RDREQ_sum"],
+                                                                         mean["TCC_BUBBLE_sum"]),
+          "| derived FETCH_SIZE formula from those terms (bytes) | %.0f | |" % fetch_formula]
+    if "FETCH_SIZE" in mean and "WRITE_SIZE" in mean:
+        L.append("| derived FETCH_SIZE / WRITE_SIZE as rocprofv3 reports them (bytes) | %.0f / %.0f | |" % (
+            1024 * mean["FETCH_SIZE"], 1024 * mean["WRITE_SIZE"]))
+    if stalls:
+        L += ["\n## Memory-side stalls (same kernel)\n", "| quantity | value |", "|---|---|",
+              "| read requests stalled on DRAM credits, %% of TCC busy cycles | %.2f |" %
+              stalls["read_dram_credit_stall_pct_of_busy"],
+              "| write requests stalled on DRAM credits, %% of TCC busy cycles | %.2f |" %
+              stalls["write_dram_credit_stall_pct_of_busy"],
+              "| mean read requests in flight per busy TCC cycle (summed over channels) | %.1f |" %
+              stalls["mean_read_requests_in_flight_per_busy_cycle"],
+              "| mean TCC-to-memory read latency, cycles | %.0f |" % stalls["mean_read_latency_cycles"]]
     with open(os.path.join(out_dir, "row_kernel_%s.md" % base), "w") as f:
         f.write("\n".join(L) + "\n")
 
+
+def workload_from_args(synth, args):
+    """The named workload, with any shape or distribution given on the command line
+    replacing its own (then named "custom")."""
+    wl = synth.WORKLOADS[args.workload]
+    over = {k: v for k, v in (("world", args.world), ("tokens", args.tokens), ("hidden", args.hidden),
+                              ("eps", args.eps), ("x_sigma", args.x_sigma), ("outlier_p", args.outlier_p),
+                              ("seed", args.seed)) if v is not None}
+    if not over:
+        return wl
+    if not (1 <= over.get("world", wl.world) <= 16 and over.get("tokens", wl.tokens) >= 1 and
+            1 <= over.get("hidden", wl.hidden) <= 65536 and over.get("eps", wl.eps) >= 0 and
+            0 <= over.get("outlier_p", wl.outlier_p) <= 1 and over.get("x_sigma", wl.x_sigma) > 0):
+        raise SystemExit("bench.py: shape or distribution out of range: %s" % over)
+    return wl.with_(name="custom", **over)
 
 
 def main():
@@ -713,32 +865,39 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-sweep", action="store_true", help="only the T=4096 headline")
     ap.add_argument("--workload", default="prefill", choices=BENCH_WORKLOADS,
-                    help="headline workload (the T sweep, fit, fusion, variant and rank-sum sections run "
-                         "only for prefill, the metric's W=4 H=2048 shape)")
+                    help="headline workload (the T sweep, fit, fusion, variant, rank-sum and ceiling sections "
+                         "run only for the unmodified prefill workload, the metric's W=4 H=2048 shape)")
+    ap.add_argument("--world", type=int, help="W: rank partials (overrides the workload's)")
+    ap.add_argument("--tokens", type=int, help="T: token rows (overrides the workload's)")
+    ap.add_argument("--hidden", type=int, help="H: hidden size (overrides the workload's)")
+    ap.add_argument("--eps", type=float, help="RMSNorm eps (overrides the workload's)")
+    ap.add_argument("--x-sigma", type=float, help="standard deviation of the partials (overrides the workload's)")
+    ap.add_argument("--outlier-p", type=float, help="fraction of partial entries scaled x100 (overrides)")
+    ap.add_argument("--seed", type=int, help="input seed (overrides the workload's)")
     ap.add_argument("--summarize", metavar="RUN_DIR",
                     help="write the profiles/ summary of the workload from rocprofv3 outputs in RUN_DIR and exit")
     args = ap.parse_args()
     if args.summarize:
         summarize_profiles(args.summarize, args.workload)
         return
-    if args.workload != "prefill":
-        args.no_sweep = True
-
     if args.gpus != 1:
         print("bench.py measures one GPU: the partial sums of all ranks are modelled as buffers already "
               "in this GPU's memory, and nothing here uses a second GPU. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    import synth
+    wl = workload_from_args(synth, args)
+    if wl.name != "prefill":
+        args.no_sweep = True
+
     import torch
     import residual_add_rmsnorm_arrms_amd as A
-    import synth
 
     if not os.path.exists(A.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
-    wl = synth.WORKLOADS[args.workload]
     W, T, H, eps = wl.world, wl.tokens, wl.hidden, wl.eps
     log("generating inputs W=%d T=%d H=%d" % (W, T, H))
     x, res, w = synth.make_inputs(wl)
@@ -746,8 +905,8 @@ def main():
     # workloads: one call per slot (each slot alone is far beyond the Infinity Cache)
     pool_rows = POOL_ROWS if 4 * T <= POOL_ROWS else T
     pool = Pool(torch, x, res, w, rows=pool_rows)
-    log("pool: %d slots, %.2f GiB" % (POOL_SLOTS, pool.nbytes / 2 ** 30))
-    op = A.FusedReduceResidualRMSNorm(max_world=max(8, W), max_tokens=pool_rows, max_hidden=H, device=0)
+    log("pool: %d slots, %.2f GiB" % (pool.slots, pool.nbytes / 2 ** 30))
+    op = A.FusedReduceResidualRMSNorm(max_world=16, max_tokens=pool_rows, max_hidden=H, device=0)
     stream = torch.cuda.current_stream().cuda_stream
 
     def caller(t):
@@ -790,8 +949,10 @@ def main():
         log("parity of the timed configuration vs oracle: %s" % parity)
 
     sweep, fit, fusion, reduce_sweep, variants, splith_regime, worlds = [], None, None, [], [], [], []
+    ceiling = None
     if not args.no_sweep:
         ctx = Ctx(torch, A, synth, op, pool, W, H, eps, stream)
+        ceiling = read_ceiling(ctx, achieved)
         sweep = sweep_tokens(ctx)
         fit = fixed_and_streaming(ctx)
         fusion, reduce_sweep = fusion_and_rank_sum(ctx, T, nbytes, gpu_ms)
@@ -806,12 +967,12 @@ def main():
     copy_same = copy_same_bytes(torch, nbytes, pairs=max(2, min(10, int(4e9 // nbytes))))
     log("copy of the headline's byte count (%d B, rotating): %.2f us, %.1f GB/s" % (
         copy_same["bytes_per_copy"], copy_same["us"], copy_same["GB_s"]))
-    tr = traffic_record(wl)
+    tr = traffic_record(wl, plan)
     op.close()
 
     value = nbytes / (wall_ms * 1e-3) / 1e9
     out = {
-        "metric": METRIC if args.workload == "prefill" else
+        "metric": METRIC if wl.name == "prefill" else
         "achieved HBM GB/s (%% of peak) and µs/call, W=%d H=%d T=%d" % (W, H, T),
         "value": value,
         "unit": "GB/s",
@@ -822,7 +983,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic (seeded SplitMix64/Box-Muller; x~N(0,%g^2)%s, residual~N(0,%g^2), weight~U(%g,%g))" % (
             wl.x_sigma, (", %g%% of x elements scaled x%g" % (100 * wl.outlier_p, wl.outlier_scale))
             if wl.outlier_p else "", wl.residual_sigma, wl.weight_lo, wl.weight_hi),
@@ -831,11 +992,14 @@ def main():
                    "world": W, "tokens": T, "hidden": H, "io_dtype": "bf16", "accumulate": "f32 rank sum, f64 "
                    "sum of squares", "algorithmic_bytes_per_call": nbytes, "plan": plan,
                    "pool_bytes": pool.nbytes, "parallelism": "1 GPU"},
-        "frac_of_peak": value / HBM_PEAK_GBS,
+        "frac_of_peak_wall": value / HBM_PEAK_GBS,
         "us_per_call": wall_ms * 1e3,
+        "timing": "value, ms_per_step, us_per_call and frac_of_peak_wall: host wall clock over the K timed "
+                  "calls between two synchronisations; roofline: HIP events on the launch stream over the same "
+                  "region",
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": (tr["fetch_bytes_per_launch"] + tr["write_bytes_per_launch"]) if tr else None,
+                     "traffic": (tr["read_bytes_per_launch"] + tr["write_bytes_per_launch"]) if tr else None,
                      "kernel_mean_us": gpu_ms * 1e3, "launches_timed": args.steps,
                      "timing": "HIP events on the launch stream around the K timed launches",
                      "event_pair_p50_us": pct(durs, 50) * 1e3, "event_pair_p90_us": pct(durs, 90) * 1e3,
@@ -851,6 +1015,7 @@ def main():
         "variants": variants,
         "splith_regime": splith_regime,
         "world_sweep": worlds,
+        "ceiling": ceiling,
         "launch_floor_graph_us": floor_us,
         "device": {"name": props.name, "compute_units": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", None), "memory_GiB": props.total_memory / 2 ** 30},
