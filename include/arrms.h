@@ -50,6 +50,7 @@ extern "C" {
 #define ARRMS_ERR_UNSUPPORTED 2 /* a valid request the selected variant cannot run */
 #define ARRMS_ERR_HIP 3         /* a HIP call failed; see arrms_last_hip_error */
 #define ARRMS_ERR_OOM 4         /* workspace allocation failed in arrms_create */
+#define ARRMS_ERR_SCRATCH 5     /* arrms_fused_noalloc: the call needs more than its static scratch */
 
 /* ---- kernel variants ----------------------------------------------------- */
 #define ARRMS_VARIANT_AUTO 0   /* choose per call from the shape (default) */
@@ -63,6 +64,7 @@ extern "C" {
 #define ARRMS_MAX_WORLD 16        /* largest W */
 #define ARRMS_MAX_HIDDEN 65536    /* largest H */
 #define ARRMS_ROW_MAX_HIDDEN 16384 /* largest H of the row variant */
+#define ARRMS_NOALLOC_SCRATCH_DOUBLES 131072 /* static split-H scratch of arrms_fused_noalloc (1 MiB per GPU) */
 
 typedef struct arrms_ctx* arrms_handle_t;
 
@@ -206,6 +208,30 @@ int arrms_reduce(arrms_handle_t h, const void* const* partials, int world, int t
 int arrms_plan_reduce(int cu_count, const arrms_tuning_t* tuning, int max_world, int max_tokens,
                       int max_hidden, const void* const* partials, int world, int tokens, int hidden,
                       const void* reduced, arrms_plan_t* plan);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, hosts that forbid hipMalloc): arrms_fused without a
+ * handle and without any allocation, on the CURRENT device (hipGetDevice) and
+ * `stream`, which must belong to it.  Arguments, layout, aliasing rules,
+ * results and error behaviour are those of arrms_fused with the automatic
+ * variant, no tuning and the largest limits (world <= ARRMS_MAX_WORLD,
+ * hidden <= ARRMS_MAX_HIDDEN, any tokens >= 0).
+ * The split-H workspace is a static device array of
+ * ARRMS_NOALLOC_SCRATCH_DOUBLES doubles that each GPU holds from its first call
+ * until the process ends; its address is looked up once per device, at that
+ * device's first call.  A call whose plan is split-H and needs more than that,
+ * tokens * chunks_per_row doubles (see arrms_plan with ARRMS_MAX_WORLD, INT_MAX
+ * tokens and ARRMS_MAX_HIDDEN as limits), returns ARRMS_ERR_SCRATCH and
+ * enqueues nothing; other plans use no scratch.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (other streams or host
+ * threads) race when they run split-H.  The array needs no clearing (each call
+ * writes every slot it reads).  Returns ARRMS_OK, ARRMS_ERR_INVALID_ARG,
+ * ARRMS_ERR_UNSUPPORTED, ARRMS_ERR_SCRATCH or ARRMS_ERR_HIP (no current device,
+ * the device set-up or the launch failed).
+ */
+int arrms_fused_noalloc(const void* const* partials, int world, int tokens, int hidden, const void* residual,
+                        const void* weight, float eps, void* residual_out, void* norm_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -28,6 +28,7 @@ ARRMS_ERR_INVALID_ARG = 1
 ARRMS_ERR_UNSUPPORTED = 2
 ARRMS_ERR_HIP = 3
 ARRMS_ERR_OOM = 4
+ARRMS_ERR_SCRATCH = 5
 
 ARRMS_VARIANT_AUTO = 0
 ARRMS_VARIANT_ROW = 1
@@ -39,11 +40,12 @@ ARRMS_VARIANT_REDUCE_SCALAR = 5
 ARRMS_MAX_WORLD = 16
 ARRMS_MAX_HIDDEN = 65536
 ARRMS_ROW_MAX_HIDDEN = 16384
+ARRMS_NOALLOC_SCRATCH_DOUBLES = 131072
 
 # Every symbol include/arrms.h declares.
 EXPORTS = ("arrms_create", "arrms_fused", "arrms_destroy", "arrms_status_string", "arrms_last_hip_error",
            "arrms_set_variant", "arrms_set_tuning", "arrms_plan", "arrms_query_plan", "arrms_reduce",
-           "arrms_plan_reduce")
+           "arrms_plan_reduce", "arrms_fused_noalloc")
 
 
 class arrms_plan_t(ctypes.Structure):
@@ -99,6 +101,7 @@ def load() -> ctypes.CDLL:
             lib.arrms_reduce.argtypes = [vp, ctypes.POINTER(vp), ci, ci, ci, vp, vp]
             lib.arrms_plan_reduce.argtypes = [ci, ctypes.POINTER(arrms_tuning_t), ci, ci, ci, ctypes.POINTER(vp), ci,
                                               ci, ci, vp, ctypes.POINTER(arrms_plan_t)]
+            lib.arrms_fused_noalloc.argtypes = [ctypes.POINTER(vp), ci, ci, ci, vp, vp, cf, vp, vp, vp]
             _lib = lib
     return _lib
 
@@ -121,6 +124,13 @@ def arrms_fused(h, partials: Optional[Sequence[int]], world: int, tokens: int, h
                 weight: int, eps: float, residual_out: int, norm_out: int, stream: int = 0) -> int:
     return load().arrms_fused(h, _ptrs(partials), world, tokens, hidden, residual, weight, eps, residual_out,
                               norm_out, stream)
+
+
+def arrms_fused_noalloc(partials: Optional[Sequence[int]], world: int, tokens: int, hidden: int, residual: int,
+                        weight: int, eps: float, residual_out: int, norm_out: int, stream: int = 0) -> int:
+    """arrms_fused without a handle or any allocation, on the current device (static scratch)."""
+    return load().arrms_fused_noalloc(_ptrs(partials), world, tokens, hidden, residual, weight, eps, residual_out,
+                                      norm_out, stream)
 
 
 def arrms_destroy(h) -> int:

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libarrms.so")
 SOURCES = [os.path.join(CSRC, "arrms_kernels.hip"), os.path.join(CSRC, "arrms_reduce.hip"),
-           os.path.join(CSRC, "arrms_api.cpp")]
+           os.path.join(CSRC, "arrms_api.cpp"), os.path.join(CSRC, "arrms_noalloc.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

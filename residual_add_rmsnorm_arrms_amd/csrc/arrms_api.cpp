@@ -271,6 +271,7 @@ const char* arrms_status_string(int status) {
         case ARRMS_ERR_UNSUPPORTED: return "unsupported shape or variant";
         case ARRMS_ERR_HIP: return "HIP runtime error";
         case ARRMS_ERR_OOM: return "out of device memory";
+        case ARRMS_ERR_SCRATCH: return "request exceeds the static scratch of the no-allocation entry point";
         default: return "unknown status";
     }
 }
@@ -428,6 +429,41 @@ int plan_reduce(int cu_count, const arrms_tuning_t* tuning, int max_world, int m
 
 }  // namespace
 
+namespace arrms {
+
+hipError_t launch_fused(const arrms_plan_t& p, const void* const* partials, int world, int tokens, int hidden,
+                        const void* residual, const void* weight, float eps, void* residual_out, void* norm_out,
+                        double* ws, hipStream_t stream) {
+    Args a;
+    memset(&a, 0, sizeof a);
+    for (int r = 0; r < world; ++r) a.x.p[r] = partials[r];
+    a.residual = residual;
+    a.weight = weight;
+    a.residual_out = residual_out;
+    a.norm_out = norm_out;
+    a.ws = ws;
+    a.hidden_d = static_cast<double>(hidden);
+    a.eps = eps;
+    a.world = world;
+    a.tokens = tokens;
+    a.hidden = hidden;
+    a.nvec = hidden / 8;
+    a.threads_per_row = p.threads_per_row;
+    a.rows_per_block = p.rows_per_block;
+    a.chunks = p.chunks_per_row;
+    a.chunk_vec = p.block * p.vec_per_thread;
+    a.blocks = p.blocks;
+    a.xcd_chunk = p.xcd_chunk;
+    switch (p.variant) {
+        case ARRMS_VARIANT_ROW: return launch_row(a, p.vec_per_thread, p.grid, p.block, stream);
+        case ARRMS_VARIANT_SPLITH: return launch_splith(a, p.vec_per_thread, p.grid, p.block, stream);
+        case ARRMS_VARIANT_SCALAR: return launch_scalar(a, p.grid, p.block, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace arrms
+
 extern "C" {
 
 int arrms_plan(int cu_count, int variant, const arrms_tuning_t* tuning, int max_world, int max_tokens,
@@ -579,27 +615,10 @@ int arrms_fused(arrms_handle_t h, const void* const* partials, int world, int to
     const int rc = arrms_query_plan(h, partials, world, tokens, hidden, residual, weight, eps, residual_out,
                                     norm_out, &p);
     if (rc != ARRMS_OK || p.grid == 0) return rc;
-
-    arrms::Args a;
-    memset(&a, 0, sizeof a);
-    for (int r = 0; r < world; ++r) a.x.p[r] = partials[r];
-    a.residual = residual;
-    a.weight = weight;
-    a.residual_out = residual_out;
-    a.norm_out = norm_out;
-    a.ws = h->ws;
-    a.hidden_d = static_cast<double>(hidden);
-    a.eps = eps;
-    a.world = world;
-    a.tokens = tokens;
-    a.hidden = hidden;
-    a.nvec = hidden / 8;
-    a.threads_per_row = p.threads_per_row;
-    a.rows_per_block = p.rows_per_block;
-    a.chunks = p.chunks_per_row;
-    a.chunk_vec = p.block * p.vec_per_thread;
-    a.blocks = p.blocks;
-    a.xcd_chunk = p.xcd_chunk;
+    // The handle's workspace holds max_tokens rows of the most chunks any call can plan.
+    if (!arrms::splith_workspace_fits(p, tokens, static_cast<long long>(h->max_tokens > 0 ? h->max_tokens : 1) *
+                                                     h->ws_chunks))
+        return ARRMS_ERR_UNSUPPORTED;
 
     int prev = -1;
     if (hipGetDevice(&prev) != hipSuccess) prev = -1;
@@ -607,12 +626,8 @@ int arrms_fused(arrms_handle_t h, const void* const* partials, int world, int to
         h->last_hip_error = static_cast<int>(hipErrorInvalidDevice);
         return ARRMS_ERR_HIP;
     }
-    hipError_t e;
-    switch (p.variant) {
-        case ARRMS_VARIANT_ROW: e = arrms::launch_row(a, p.vec_per_thread, p.grid, p.block, stream); break;
-        case ARRMS_VARIANT_SPLITH: e = arrms::launch_splith(a, p.vec_per_thread, p.grid, p.block, stream); break;
-        default: e = arrms::launch_scalar(a, p.grid, p.block, stream); break;
-    }
+    const hipError_t e = arrms::launch_fused(p, partials, world, tokens, hidden, residual, weight, eps, residual_out,
+                                             norm_out, h->ws, stream);
     if (prev >= 0 && prev != h->device) (void)hipSetDevice(prev);
     if (e != hipSuccess) {
         h->last_hip_error = static_cast<int>(e);

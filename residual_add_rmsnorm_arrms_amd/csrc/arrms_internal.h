@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "arrms.h"
+
 namespace arrms {
 
 constexpr int kMaxWorld = 16;
@@ -151,5 +153,19 @@ hipError_t launch_scalar(const Args& a, int grid, int block, hipStream_t s);
 // for W <= 8, only 1 for the 16-wide rank arrays of larger W (register budget).
 hipError_t launch_reduce(const Args& a, int vec_per_thread, int grid, int block, hipStream_t s);
 hipError_t launch_reduce_scalar(const Args& a, int grid, int block, hipStream_t s);
+
+// Does a planned call's split-H workspace, tokens x chunks_per_row doubles, fit
+// a workspace of `capacity` doubles?  Plans of the other variants use none.
+inline bool splith_workspace_fits(const arrms_plan_t& p, int tokens, long long capacity) {
+    return p.variant != ARRMS_VARIANT_SPLITH ||
+           (p.chunks_per_row > 0 && static_cast<long long>(tokens) * p.chunks_per_row <= capacity);
+}
+
+// Launch a planned fused call (plan from arrms_plan) on `stream` of the current
+// device; `ws` is the split-H workspace (at least tokens x chunks_per_row doubles
+// for a split-H plan, unused otherwise).  Returns the hipError_t of the launch.
+hipError_t launch_fused(const arrms_plan_t& p, const void* const* partials, int world, int tokens, int hidden,
+                        const void* residual, const void* weight, float eps, void* residual_out, void* norm_out,
+                        double* ws, hipStream_t stream);
 
 }  // namespace arrms

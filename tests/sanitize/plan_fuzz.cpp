@@ -81,6 +81,22 @@ int main(int argc, char** argv) {
             }
             if (p.xcd_chunk && p.grid % (8 * p.xcd_chunk)) return fail("xcd grid", i);
         }
+        // The no-allocation entry point's plan (automatic, no tuning, absolute limits):
+        // every plan it accepts keeps the split-H workspace index, row * chunks + chunk
+        // for row < T, inside its static scratch.
+        arrms_plan_t q;
+        const int rcs = arrms_plan(cu > 0 ? cu : 1, ARRMS_VARIANT_AUTO, nullptr, ARRMS_MAX_WORLD, 0x7fffffff,
+                                   ARRMS_MAX_HIDDEN, parts, W, T, H, res, w, eps, ro, no, &q);
+        if (rcs == ARRMS_OK && T > 0 && q.grid > 0 &&
+            arrms::splith_workspace_fits(q, T, ARRMS_NOALLOC_SCRATCH_DOUBLES)) {
+            if (q.variant == ARRMS_VARIANT_SPLITH &&
+                ((long long)q.blocks > ARRMS_NOALLOC_SCRATCH_DOUBLES || q.blocks != T * q.chunks_per_row))
+                return fail("static scratch bound", i);
+        }
+        if (rcs == ARRMS_OK && T > 0 && q.variant == ARRMS_VARIANT_SPLITH &&
+            (long long)T * q.chunks_per_row > ARRMS_NOALLOC_SCRATCH_DOUBLES &&
+            arrms::splith_workspace_fits(q, T, ARRMS_NOALLOC_SCRATCH_DOUBLES))
+            return fail("static scratch accepted", i);
         const int rc2 = arrms_plan_reduce(cu, tp, maxw, maxt, maxh, parts, W, T, H, no, &p);
         if (rc2 == ARRMS_OK && T > 0 && p.grid > 0) {
             const long long count = (long long)T * H;

@@ -60,6 +60,7 @@ def test_status_strings():
     assert A.arrms_status_string(A.ARRMS_ERR_UNSUPPORTED) == "unsupported shape or variant"
     assert A.arrms_status_string(A.ARRMS_ERR_HIP) == "HIP runtime error"
     assert A.arrms_status_string(A.ARRMS_ERR_OOM) == "out of device memory"
+    assert "static scratch" in A.arrms_status_string(A.ARRMS_ERR_SCRATCH)
     assert A.arrms_status_string(99) == "unknown status"
 
 
