@@ -563,6 +563,37 @@ def forced_variants(ctx):
     return variants
 
 
+def scalar_widths(ctx, T=4096):
+    """The scalar variant (rows the 16-byte kernels cannot take) at W=4 T=4096: rows of
+    H = 2044, 2046 and 2047 elements (8-, 4- and 2-byte loads chosen automatically) on
+    the prefill pool's buffers read with that row length, and H = 2048 forced through
+    the scalar kernel with each load width.  Back-to-back GPU time."""
+    torch, A, op, W = ctx.torch, ctx.A, ctx.op, ctx.W
+    sets = ctx.pool.sets(T)  # row length below 2048 stays inside each 2048-element row slot
+    out = []
+    cases = [(2044, None), (2046, None), (2047, None), (2048, 4), (2048, 2), (2048, 1)]
+    for H, elems in cases:
+        if elems:
+            op.set_variant(A.ARRMS_VARIANT_SCALAR)
+            op.set_tuning(scalar_elems=elems)
+        c = Caller(A, op.handle, sets, W, T, H, ctx.pool.weight.data_ptr(), ctx.eps, ctx.stream)
+        s0 = ctx.pool.slot[0]
+        view = lambda k: s0[k].view(-1)[:T * H].view(T, H)
+        p = op.plan([view(r) for r in range(W)], view(W), ctx.pool.weight[:H], ctx.eps, view(W + 1), view(W + 2))
+        for _ in range(50):
+            c()
+        _, g = time_back_to_back(torch, c, 500)
+        op.set_variant(A.ARRMS_VARIANT_AUTO)
+        op.set_tuning()
+        b = algorithmic_bytes(W, T, H)
+        out.append({"W": W, "T": T, "H": H, "forced": bool(elems), "variant": VARIANT_NAMES[p["variant"]],
+                    "elems_per_load": p["elems_per_load"], "us": g * 1e3, "GB_s": b / (g * 1e-3) / 1e9,
+                    "frac_of_peak_gpu_events": b / (g * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        log("scalar W=%d T=%d H=%d%s: %d-byte loads, %.2f us, %.0f GB/s" % (
+            W, T, H, " (forced)" if elems else "", 2 * p["elems_per_load"], g * 1e3, b / (g * 1e-3) / 1e9))
+    return out
+
+
 def world_sweep(ctx, T=4096, worlds=(1, 2, 3, 4, 6, 8, 12, 16)):
     """The fused call at H=2048 T=4096 across rank counts (the shapes of other
     tensor-parallel degrees): back-to-back GPU time and achieved bandwidth, each W
@@ -949,7 +980,7 @@ def main():
         log("parity of the timed configuration vs oracle: %s" % parity)
 
     sweep, fit, fusion, reduce_sweep, variants, splith_regime, worlds = [], None, None, [], [], [], []
-    ceiling = None
+    ceiling, scalar = None, []
     if not args.no_sweep:
         ctx = Ctx(torch, A, synth, op, pool, W, H, eps, stream)
         ceiling = read_ceiling(ctx, achieved)
@@ -957,6 +988,7 @@ def main():
         fit = fixed_and_streaming(ctx)
         fusion, reduce_sweep = fusion_and_rank_sum(ctx, T, nbytes, gpu_ms)
         variants = forced_variants(ctx)
+        scalar = scalar_widths(ctx)
         splith_regime = splith_crossover(ctx)
         worlds = world_sweep(ctx)
 
@@ -1013,6 +1045,7 @@ def main():
         "copy_context": copy,
         "copy_same_bytes": copy_same,
         "variants": variants,
+        "scalar_widths": scalar,
         "splith_regime": splith_regime,
         "world_sweep": worlds,
         "ceiling": ceiling,

@@ -56,7 +56,7 @@ extern "C" {
 #define ARRMS_VARIANT_AUTO 0   /* choose per call from the shape (default) */
 #define ARRMS_VARIANT_ROW 1    /* one token row per workgroup (or per lane group) */
 #define ARRMS_VARIANT_SPLITH 2 /* each row split over several workgroups, two kernels */
-#define ARRMS_VARIANT_SCALAR 3 /* element-wise loads: any H, any 2-byte alignment */
+#define ARRMS_VARIANT_SCALAR 3 /* 8-, 4- or 2-byte loads: any H, any 2-byte alignment */
 /* Plan kinds of arrms_reduce (the rank sum alone). */
 #define ARRMS_VARIANT_REDUCE 4        /* 16-byte vector loads, flat over T*H elements */
 #define ARRMS_VARIANT_REDUCE_SCALAR 5 /* element-wise, any 2-byte alignment */
@@ -80,6 +80,7 @@ typedef struct {
     int kernels;         /* kernel launches per call: 2 for split-H, else 1 (0: none) */
     int blocks;          /* logical workgroups per kernel (grid minus padding of the XCD mapping) */
     int xcd_chunk;       /* K > 0: runs of K consecutive workgroups (rows) kept on one XCD; 0: hardware order */
+    int elems_per_load;  /* scalar: BF16 elements per load (4, 2 or 1: 8-, 4- or 2-byte loads); else 0 */
 } arrms_plan_t;
 
 /* Optional tuning overrides; 0 (or -1 where stated) keeps the automatic choice.
@@ -91,6 +92,7 @@ typedef struct {
     int splith_max_tokens; /* automatic variant uses split-H when tokens <= this; -1 automatic */
     int xcd_chunk;         /* -1 automatic; 0 hardware round-robin; K > 0 runs of K blocks per XCD */
     int rows_per_block;    /* row: token rows per workgroup (power of two); 0 automatic */
+    int scalar_elems;      /* scalar: at most this many BF16 elements per load (1, 2 or 4); 0 automatic */
 } arrms_tuning_t;
 
 /*
@@ -131,7 +133,9 @@ int arrms_create(arrms_handle_t* out, int device, int max_world, int max_tokens,
  * Pointers must be 2-byte aligned.  Outputs may not overlap each other or any
  * input, except residual_out == residual.  Inputs may overlap each other.
  * H a multiple of 8 with every pointer 16-byte aligned uses the vector kernels;
- * anything else uses the scalar kernel with the same results.
+ * anything else uses the scalar kernel with the same results, with loads of 4
+ * BF16 elements when H % 4 == 0 and every pointer is 8-byte aligned, of 2 when
+ * H is even and every pointer 4-byte aligned, else of 1.
  * All checks happen before anything is enqueued: an error has no side effect.
  * Returns ARRMS_OK, ARRMS_ERR_INVALID_ARG, ARRMS_ERR_UNSUPPORTED (a forced
  * variant cannot run this shape, or the launch would exceed 2^32 - 1 work-items,

@@ -86,6 +86,8 @@ bool valid_tuning(const arrms_tuning_t* t) {
     if (t->xcd_chunk < -1) return false;
     const int rp = t->rows_per_block;
     if (rp < 0 || rp > 64 || (rp & (rp - 1))) return false;
+    const int se = t->scalar_elems;
+    if (!(se == 0 || se == 1 || se == 2 || se == 4)) return false;
     return true;
 }
 
@@ -225,11 +227,16 @@ int plan_splith(int cu_count, int max_hidden, int world, int tokens, int hidden,
     return ARRMS_OK;
 }
 
-// One row per workgroup, kScalarSpan (8) elements per lane per span: enough
-// whole waves to cover the row in one span, at most 1024 lanes.
-void plan_scalar(int tokens, int hidden, arrms_plan_t* p) {
+// Scalar plan: one row per workgroup, 8 elements per lane per span: enough whole
+// waves to cover the row in one span, at most 1024 lanes (512 for more than 8
+// ranks: the kernels' __launch_bounds__).  Loads are `elems` BF16
+// elements wide (the widest that H and every pointer's alignment allow, at most
+// the tuned width).  XCD runs as in the row variant (about 3 MiB of traffic per run).
+void plan_scalar(int world, int tokens, int hidden, int elems, const arrms_tuning_t* t, arrms_plan_t* p) {
+    const int max_block = world > 8 ? 512 : 1024;
     int block = ((hidden + 7) / 8 + 63) / 64 * 64;
-    if (block > 1024) block = 1024;
+    if (block > max_block) block = max_block;
+    if (t && t->scalar_elems && t->scalar_elems < elems) elems = t->scalar_elems;
     p->variant = ARRMS_VARIANT_SCALAR;
     p->vec_per_thread = 0;
     p->threads_per_row = block;
@@ -237,9 +244,22 @@ void plan_scalar(int tokens, int hidden, arrms_plan_t* p) {
     p->chunks_per_row = 1;
     p->block = block;
     p->blocks = tokens;
-    p->grid = tokens;
     p->kernels = 1;
-    p->xcd_chunk = 0;
+    p->elems_per_load = elems;
+    int k = 0;
+    if (p->blocks >= 64) {
+        const long row_bytes = 2L * (world + 3) * hidden;
+        k = 1;
+        while (2L * k * row_bytes <= kXcdRunBytes) k *= 2;
+    }
+    finish_vector_plan(t, p, k);
+}
+
+// Widest load, in BF16 elements, that H and the OR of all pointer addresses allow.
+int scalar_elems(int hidden, uintptr_t any) {
+    if (hidden % 4 == 0 && (any & 7u) == 0) return 4;
+    if (hidden % 2 == 0 && (any & 3u) == 0) return 2;
+    return 1;
 }
 
 // Automatic crossover to split-H, measured on MI355X with HIP-graph replay (GPU
@@ -329,9 +349,10 @@ int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
             return ARRMS_ERR_INVALID_ARG;
 
     const bool vector_ok = (hidden % 8 == 0) && ((any & 15u) == 0);
+    const int elems = scalar_elems(hidden, any);
     switch (variant) {
         case ARRMS_VARIANT_SCALAR:
-            plan_scalar(tokens, hidden, plan);
+            plan_scalar(world, tokens, hidden, elems, tuning, plan);
             return ARRMS_OK;
         case ARRMS_VARIANT_ROW:
             if (!vector_ok || hidden > ARRMS_ROW_MAX_HIDDEN) return ARRMS_ERR_UNSUPPORTED;
@@ -343,7 +364,7 @@ int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
             break;
     }
     if (!vector_ok) {
-        plan_scalar(tokens, hidden, plan);
+        plan_scalar(world, tokens, hidden, elems, tuning, plan);
         return ARRMS_OK;
     }
     int split_max = (tuning && tuning->splith_max_tokens >= 0) ? tuning->splith_max_tokens
@@ -360,7 +381,7 @@ int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
     memset(plan, 0, sizeof *plan);
     if (plan_splith(cu_count, max_hidden, world, tokens, hidden, tuning, plan) == ARRMS_OK) return ARRMS_OK;
     memset(plan, 0, sizeof *plan);
-    plan_scalar(tokens, hidden, plan);
+    plan_scalar(world, tokens, hidden, elems, tuning, plan);
     return ARRMS_OK;
 }
 
@@ -454,6 +475,7 @@ hipError_t launch_fused(const arrms_plan_t& p, const void* const* partials, int 
     a.chunk_vec = p.block * p.vec_per_thread;
     a.blocks = p.blocks;
     a.xcd_chunk = p.xcd_chunk;
+    a.elems_per_load = p.elems_per_load;
     switch (p.variant) {
         case ARRMS_VARIANT_ROW: return launch_row(a, p.vec_per_thread, p.grid, p.block, stream);
         case ARRMS_VARIANT_SPLITH: return launch_splith(a, p.vec_per_thread, p.grid, p.block, stream);

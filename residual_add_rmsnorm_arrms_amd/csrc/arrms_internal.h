@@ -40,6 +40,7 @@ struct Args {
     int chunk_vec;          // split-H: vectors per chunk
     int blocks;             // logical workgroups (the launched grid may add XCD padding)
     int xcd_chunk;          // K > 0: runs of K consecutive blocks per XCD (grid a multiple of 8K)
+    int elems_per_load;     // scalar: BF16 elements per load (1, 2 or 4)
     long long count;        // rank sum only: elements (tokens * hidden)
 };
 
@@ -102,7 +103,8 @@ struct SplitNormArgs {
     uint32_t shape;
 };
 
-// Element-wise variant.  shape: bits 0-15 lanes per workgroup, 16-20 W.
+// Scalar variant (narrow loads, one row per workgroup).  shape: bits 0-16 H,
+// 17-21 lanes per workgroup / 64, 22-26 W, 27-28 log2(elements per load).
 template <int WA>
 struct ScalarArgs {
     Ptrs<WA> x;
@@ -111,7 +113,8 @@ struct ScalarArgs {
     void* residual_out;
     void* norm_out;
     float eps;
-    int hidden;
+    int tokens;
+    int xcd_chunk;
     uint32_t shape;
 };
 

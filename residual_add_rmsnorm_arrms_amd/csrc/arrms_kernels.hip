@@ -197,62 +197,133 @@ __global__ void __launch_bounds__(1024) splith_norm_kernel(const SplitNormArgs a
 }
 
 // -------------------------------------------------------------- scalar variant
-// Any H and any 2-byte alignment: one row per workgroup of n lanes (n <= 1024).
-// The row is walked in spans of kScalarSpan * n elements; in a span, lane l owns
-// elements l, l + n, ..., l + (kScalarSpan - 1) * n, so each 2-byte load
-// instruction of a wave covers 128 contiguous bytes.  Indexes past H are clamped
-// for loads (which stay inside the row, in one basic block, so the compiler can
-// issue the span's loads of every rank together) and masked for stores and for
-// the sum of squares.  When the row fits one span, residual_out stays in
-// registers for the second pass; otherwise the second pass re-reads it (each
-// element is read back by the lane that stored it, after the barrier).
+// Rows that the 16-byte kernels cannot take (H % 8 != 0, or a pointer not 16-byte
+// aligned).  Loads are E BF16 elements wide (E = 4, 2 or 1: 8-, 4- or 2-byte
+// loads), the widest that H and the alignment of every pointer allow.  One row per
+// workgroup of n lanes (n <= 1024, or 512 for more than 8 ranks), XCD runs as in
+// the row variant.  The row is
+// walked in spans of kScalarSpan * n elements; in a span lane l owns the E-element
+// groups l, l + n, ..., l + (8 / E - 1) * n, so each load instruction of a wave
+// covers 128 * E contiguous bytes and a lane moves 16 bytes per input per span,
+// as in the row variant.  Group indexes past the row are clamped for loads (which
+// then stay inside the row, in one basic block, so the compiler issues the span's
+// loads of every rank together) and masked for stores and for the sum of squares.
+// When the row fits one span, residual_out stays in registers for the second pass;
+// otherwise the second pass re-reads it (each group is read back by the lane that
+// stored it, after the barrier).
 constexpr int kScalarSpan = 8;
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Storage of E consecutive BF16 elements, and access to element k of it.
+template <int E> struct Group;
+template <> struct Group<1> {
+    typedef uint16_t T;
+    static __device__ __forceinline__ float get(T g, int) { return lo_f32(g); }
+};
+template <> struct Group<2> {
+    typedef uint32_t T;
+    static __device__ __forceinline__ float get(T g, int k) { return k ? hi_f32(g) : lo_f32(g); }
+};
+template <> struct Group<4> {
+    typedef u32x2 T;
+    static __device__ __forceinline__ float get(T g, int k) { return (k & 1) ? hi_f32(g[k >> 1]) : lo_f32(g[k >> 1]); }
+};
+
+// E binary32 values rounded to BF16 and packed as one group (element 0 lowest).
+template <int E>
+__device__ __forceinline__ typename Group<E>::T pack(const float (&v)[E]) {
+    if constexpr (E == 1) {
+        return cvt1(v[0]);
+    } else if constexpr (E == 2) {
+        return cvt2(v[0], v[1]);
+    } else {
+        return u32x2{cvt2(v[0], v[1]), cvt2(v[2], v[3])};
+    }
+}
+
+// Largest workgroup of a scalar kernel: the generic-W instances keep up to 16 ranks'
+// loads in registers and get the larger register budget of 512-lane workgroups.  The
+// host planner uses the same limits.
 template <int W>
-__global__ void __launch_bounds__(1024) scalar_kernel(const ScalarArgs<(W > 0 ? W : kMaxWorld)> a) {
-    const int world = W > 0 ? W : static_cast<int>((a.shape >> 16) & 31u);
-    const int row = blockIdx.x;
+constexpr int scalar_max_threads() { return W == 0 ? 512 : 1024; }
+
+template <int W, int E>
+__global__ void __launch_bounds__(scalar_max_threads<W>()) scalar_kernel(const ScalarArgs<(W > 0 ? W : kMaxWorld)> a) {
+    typedef typename Group<E>::T G;
+    constexpr int S = kScalarSpan / E;  // groups per lane per input in a span
+    const int world = W > 0 ? W : static_cast<int>((a.shape >> 22) & 31u);
+    const int row = logical_block(a.xcd_chunk, a.tokens);
+    if (row < 0) return;  // padding workgroup of the XCD mapping (whole workgroup)
     const int tid = threadIdx.x;
-    const int n = static_cast<int>(a.shape & 0xffffu);  // the workgroup size
-    const int H = a.hidden;
-    const int span = kScalarSpan * n;
-    const size_t base = static_cast<size_t>(row) * static_cast<size_t>(H);
-    const uint16_t* res = static_cast<const uint16_t*>(a.residual) + base;
-    const uint16_t* w = static_cast<const uint16_t*>(a.weight);
-    uint16_t* ro_out = static_cast<uint16_t*>(a.residual_out) + base;
-    uint16_t* n_out = static_cast<uint16_t*>(a.norm_out) + base;
+    const int n = static_cast<int>((a.shape >> 17) & 31u) * 64;  // the workgroup size
+    const int H = static_cast<int>(a.shape & 0x1ffffu);
+    const int ng = H / E;  // groups per row
+    const int span = S * n;
+    const size_t base = static_cast<size_t>(row) * static_cast<size_t>(ng);
+    const G* res = static_cast<const G*>(a.residual) + base;
+    const G* w = static_cast<const G*>(a.weight);
+    G* ro_out = static_cast<G*>(a.residual_out) + base;
+    G* n_out = static_cast<G*>(a.norm_out) + base;
 
     double ss = 0.0;
-    uint16_t keep[kScalarSpan];  // residual_out of the last span
-    uint16_t wk[kScalarSpan];    // weight of the first span, loaded with the first span's inputs
-    for (int h0 = 0; h0 < H; h0 += span) {
-        float acc[kScalarSpan];
-        uint16_t rs[kScalarSpan];
-        const uint16_t* x0 = static_cast<const uint16_t*>(a.x.p[0]) + base;
+    G keep[S];  // residual_out of the last span
+    G wk[S];    // weight of the last span, loaded with its inputs (no branch between the loads)
+    // Ranks whose loads the span keeps in registers: all W of a specialised kernel;
+    // the generic kernel (up to 16 ranks, W known at run time) adds the ranks after
+    // x_0 one at a time instead, which keeps its registers within budget.
+    constexpr int WL = W > 0 ? W : 1;
+    for (int g0 = 0; g0 < ng; g0 += span) {
+        // every load of the span first (the ranks kept, residual, weight), then the arithmetic
+        G xv[WL][S];
+        G rs[S];
 #pragma unroll
-        for (int u = 0; u < kScalarSpan; ++u) {
-            const int h = min(h0 + u * n + tid, H - 1);
-            acc[u] = lo_f32(x0[h]);
-            rs[u] = res[h];
-            if (h0 == 0) wk[u] = w[h];
+        for (int u = 0; u < S; ++u) {
+            const int g = min(g0 + u * n + tid, ng - 1);
+#pragma unroll
+            for (int r = 0; r < WL; ++r) xv[r][u] = __builtin_nontemporal_load(static_cast<const G*>(a.x.p[r]) + base + g);
+            rs[u] = __builtin_nontemporal_load(res + g);
+            wk[u] = w[g];
         }
-        // rank order 0, 1, ..., W-1 for every element
+        // binary32 rank sums, rank order 0, 1, ..., W-1 for every element
+        float acc[S][E];
 #pragma unroll
-        for (int r = 1; r < (W > 0 ? W : kMaxWorld); ++r) {
-            if (W == 0 && r >= world) break;
-            const uint16_t* xr = static_cast<const uint16_t*>(a.x.p[r]) + base;
+        for (int u = 0; u < S; ++u) {
 #pragma unroll
-            for (int u = 0; u < kScalarSpan; ++u) acc[u] = acc[u] + lo_f32(xr[min(h0 + u * n + tid, H - 1)]);
+            for (int k = 0; k < E; ++k) {
+                acc[u][k] = Group<E>::get(xv[0][u], k);
+#pragma unroll
+                for (int r = 1; r < WL; ++r) acc[u][k] = acc[u][k] + Group<E>::get(xv[r][u], k);
+            }
+        }
+        if constexpr (W == 0) {
+            for (int r = 1; r < world; ++r) {
+                const G* xr = static_cast<const G*>(a.x.p[r]) + base;
+                G v[S];
+#pragma unroll
+                for (int u = 0; u < S; ++u) v[u] = __builtin_nontemporal_load(xr + min(g0 + u * n + tid, ng - 1));
+#pragma unroll
+                for (int u = 0; u < S; ++u)
+#pragma unroll
+                    for (int k = 0; k < E; ++k) acc[u][k] = acc[u][k] + Group<E>::get(v[u], k);
+            }
         }
 #pragma unroll
-        for (int u = 0; u < kScalarSpan; ++u) {
-            const int h = h0 + u * n + tid;
-            const uint16_t o = cvt1(lo_f32(cvt1(acc[u])) + lo_f32(rs[u]));
-            keep[u] = o;
-            if (h < H) {
-                ro_out[h] = o;
-                const double d = static_cast<double>(lo_f32(o));
-                ss = __builtin_fma(d, d, ss);
+        for (int u = 0; u < S; ++u) {
+            const int g = g0 + u * n + tid;
+            const G rg = pack<E>(acc[u]);
+            float o[E];
+#pragma unroll
+            for (int k = 0; k < E; ++k) o[k] = Group<E>::get(rg, k) + Group<E>::get(rs[u], k);
+            const G og = pack<E>(o);
+            keep[u] = og;
+            if (g < ng) {
+                ro_out[g] = og;
+#pragma unroll
+                for (int k = 0; k < E; ++k) {
+                    const double d = static_cast<double>(Group<E>::get(og, k));
+                    ss = __builtin_fma(d, d, ss);
+                }
             }
         }
     }
@@ -264,26 +335,32 @@ __global__ void __launch_bounds__(1024) scalar_kernel(const ScalarArgs<(W > 0 ? 
     for (int i = 1; i < (n >> 6); ++i) total = total + wave_ss[i];
     const float inv = inv_rms(total, static_cast<double>(H), a.eps);
 
-    if (H <= span) {
+    if (ng <= span) {
 #pragma unroll
-        for (int u = 0; u < kScalarSpan; ++u) {
-            const int h = u * n + tid;
-            if (h < H) n_out[h] = cvt1((lo_f32(keep[u]) * inv) * lo_f32(wk[u]));
+        for (int u = 0; u < S; ++u) {
+            const int g = u * n + tid;
+            float v[E];
+#pragma unroll
+            for (int k = 0; k < E; ++k) v[k] = (Group<E>::get(keep[u], k) * inv) * Group<E>::get(wk[u], k);
+            if (g < ng) __builtin_nontemporal_store(pack<E>(v), n_out + g);
         }
         return;
     }
-    for (int h0 = 0; h0 < H; h0 += span) {
-        uint16_t rv[kScalarSpan], wv[kScalarSpan];
+    for (int g0 = 0; g0 < ng; g0 += span) {
+        G rv[S], wv[S];
 #pragma unroll
-        for (int u = 0; u < kScalarSpan; ++u) {
-            const int h = min(h0 + u * n + tid, H - 1);
-            rv[u] = ro_out[h];
-            wv[u] = w[h];
+        for (int u = 0; u < S; ++u) {
+            const int g = min(g0 + u * n + tid, ng - 1);
+            rv[u] = ro_out[g];
+            wv[u] = w[g];
         }
 #pragma unroll
-        for (int u = 0; u < kScalarSpan; ++u) {
-            const int h = h0 + u * n + tid;
-            if (h < H) n_out[h] = cvt1((lo_f32(rv[u]) * inv) * lo_f32(wv[u]));
+        for (int u = 0; u < S; ++u) {
+            const int g = g0 + u * n + tid;
+            float v[E];
+#pragma unroll
+            for (int k = 0; k < E; ++k) v[k] = (Group<E>::get(rv[u], k) * inv) * Group<E>::get(wv[u], k);
+            if (g < ng) __builtin_nontemporal_store(pack<E>(v), n_out + g);
         }
     }
 }
@@ -340,7 +417,11 @@ hipError_t launch_splith_partial_with(const void* fn, const Args& a, int grid, i
 
 template <int WA>
 hipError_t launch_scalar_with(const void* fn, const Args& a, int grid, int block, hipStream_t s) {
-    if (block > 0xffff || a.world > 31) return hipErrorInvalidValue;
+    const int e_code = a.elems_per_load == 4 ? 2 : (a.elems_per_load == 2 ? 1 : 0);
+    if (block % 64 || block < 64 || block > (WA > 8 ? 512 : 1024) || a.world > 31 || a.hidden < 1 ||
+        a.hidden > 0x1ffff ||
+        (1 << e_code) != a.elems_per_load || a.hidden % a.elems_per_load)
+        return hipErrorInvalidValue;
     ScalarArgs<WA> r{};
     r.x = pack_ptrs<WA>(a);
     r.residual = a.residual;
@@ -348,8 +429,10 @@ hipError_t launch_scalar_with(const void* fn, const Args& a, int grid, int block
     r.residual_out = a.residual_out;
     r.norm_out = a.norm_out;
     r.eps = a.eps;
-    r.hidden = a.hidden;
-    r.shape = static_cast<uint32_t>(block) | static_cast<uint32_t>(a.world) << 16;
+    r.tokens = a.tokens;
+    r.xcd_chunk = a.xcd_chunk;
+    r.shape = static_cast<uint32_t>(a.hidden) | static_cast<uint32_t>(block / 64) << 17 |
+              static_cast<uint32_t>(a.world) << 22 | static_cast<uint32_t>(e_code) << 27;
     return launch_with(fn, r, grid, block, s);
 }
 
@@ -461,18 +544,39 @@ hipError_t launch_splith(const Args& a, int vpt, int grid, int block, hipStream_
     return launch_with(reinterpret_cast<const void*>(&splith_norm_kernel), n, grid, block, s);
 }
 
+template <int E>
+const void* scalar_fn(int world) {
+    switch (world) {
+        case 1: return reinterpret_cast<const void*>(&scalar_kernel<1, E>);
+        case 2: return reinterpret_cast<const void*>(&scalar_kernel<2, E>);
+        case 3: return reinterpret_cast<const void*>(&scalar_kernel<3, E>);
+        case 4: return reinterpret_cast<const void*>(&scalar_kernel<4, E>);
+        case 5: return reinterpret_cast<const void*>(&scalar_kernel<5, E>);
+        case 6: return reinterpret_cast<const void*>(&scalar_kernel<6, E>);
+        case 7: return reinterpret_cast<const void*>(&scalar_kernel<7, E>);
+        case 8: return reinterpret_cast<const void*>(&scalar_kernel<8, E>);
+        default: return reinterpret_cast<const void*>(&scalar_kernel<0, E>);
+    }
+}
+
 hipError_t launch_scalar(const Args& a, int grid, int block, hipStream_t s) {
+    const void* fn = nullptr;
+    switch (a.elems_per_load) {
+        case 1: fn = scalar_fn<1>(a.world); break;
+        case 2: fn = scalar_fn<2>(a.world); break;
+        case 4: fn = scalar_fn<4>(a.world); break;
+        default: return hipErrorInvalidValue;
+    }
     switch (a.world) {
-        case 1: return launch_scalar_with<1>(reinterpret_cast<const void*>(&scalar_kernel<1>), a, grid, block, s);
-        case 2: return launch_scalar_with<2>(reinterpret_cast<const void*>(&scalar_kernel<2>), a, grid, block, s);
-        case 3: return launch_scalar_with<3>(reinterpret_cast<const void*>(&scalar_kernel<3>), a, grid, block, s);
-        case 4: return launch_scalar_with<4>(reinterpret_cast<const void*>(&scalar_kernel<4>), a, grid, block, s);
-        case 5: return launch_scalar_with<5>(reinterpret_cast<const void*>(&scalar_kernel<5>), a, grid, block, s);
-        case 6: return launch_scalar_with<6>(reinterpret_cast<const void*>(&scalar_kernel<6>), a, grid, block, s);
-        case 7: return launch_scalar_with<7>(reinterpret_cast<const void*>(&scalar_kernel<7>), a, grid, block, s);
-        case 8: return launch_scalar_with<8>(reinterpret_cast<const void*>(&scalar_kernel<8>), a, grid, block, s);
-        default:
-            return launch_scalar_with<kMaxWorld>(reinterpret_cast<const void*>(&scalar_kernel<0>), a, grid, block, s);
+        case 1: return launch_scalar_with<1>(fn, a, grid, block, s);
+        case 2: return launch_scalar_with<2>(fn, a, grid, block, s);
+        case 3: return launch_scalar_with<3>(fn, a, grid, block, s);
+        case 4: return launch_scalar_with<4>(fn, a, grid, block, s);
+        case 5: return launch_scalar_with<5>(fn, a, grid, block, s);
+        case 6: return launch_scalar_with<6>(fn, a, grid, block, s);
+        case 7: return launch_scalar_with<7>(fn, a, grid, block, s);
+        case 8: return launch_scalar_with<8>(fn, a, grid, block, s);
+        default: return launch_scalar_with<kMaxWorld>(fn, a, grid, block, s);
     }
 }
 

@@ -75,7 +75,14 @@ int main(int argc, char** argv) {
                 if (p.blocks != T * p.chunks_per_row) return fail("split blocks", i);
                 if (p.chunks_per_row > (((maxh + 7) / 8 + 63) / 64)) return fail("workspace", i);
             } else if (p.variant == ARRMS_VARIANT_SCALAR) {
-                if (p.grid != T) return fail("scalar grid", i);
+                if (p.blocks != T) return fail("scalar blocks", i);
+                const int e = p.elems_per_load;
+                if (!(e == 1 || e == 2 || e == 4) || H % e) return fail("scalar load width", i);
+                uintptr_t any = (uintptr_t)res | (uintptr_t)w | (uintptr_t)ro | (uintptr_t)no;
+                for (int r = 0; r < W; ++r) any |= (uintptr_t)parts[r];
+                if (any & (uintptr_t)(2 * e - 1)) return fail("scalar load alignment", i);
+                if ((long)p.block * 8 < H && p.block != (W > 8 ? 512 : 1024)) return fail("scalar span", i);
+                if (p.block > (W > 8 ? 512 : 1024)) return fail("scalar block", i);
             } else {
                 return fail("variant", i);
             }

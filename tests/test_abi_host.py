@@ -148,8 +148,10 @@ def test_xcd_mapping_plans():
     assert p["xcd_chunk"] == 125 and p["grid"] == 1000
     rc, p = plan(4, 3, 2048)
     assert p["xcd_chunk"] == 0 and p["grid"] == 3                       # small grids: no padding
-    rc, p = plan(4, 100, 1001)
-    assert p["variant"] == A.ARRMS_VARIANT_SCALAR and p["xcd_chunk"] == 0 and p["grid"] == 100
+    rc, p = plan(4, 100, 1001)                                          # scalar: XCD runs like the row kernel
+    assert p["variant"] == A.ARRMS_VARIANT_SCALAR and p["xcd_chunk"] == 13 and p["grid"] == 104
+    rc, p = plan(4, 63, 1001)
+    assert p["variant"] == A.ARRMS_VARIANT_SCALAR and p["xcd_chunk"] == 0 and p["grid"] == 63
 
 
 @pytest.mark.parametrize("blocks,k", [(8, 1), (13, 1), (100, 3), (64, 8), (1000, 16), (4096, 512), (77, 10)])
@@ -339,6 +341,36 @@ def test_rows_per_block_tuning():
     assert rc == A.ARRMS_OK and p["rows_per_block"] == 4 and p["block"] == 1024 and p["blocks"] == 1024
     rc, p = plan(4, 4096, 2048, variant=A.ARRMS_VARIANT_ROW, tuning=A.arrms_tuning_t.make(rows_per_block=8))
     assert rc == A.ARRMS_ERR_UNSUPPORTED                      # 2048 threads per workgroup
+
+
+@pytest.mark.parametrize("H,offset,elems", [
+    (2044, 0, 4), (5122, 0, 2), (1001, 0, 1), (2046, 0, 2),            # H decides
+    (2048, 8, 4), (2048, 4, 2), (2048, 2, 1), (2044, 4, 2), (5122, 2, 1),  # a pointer's alignment decides
+])
+@pytest.mark.parametrize("field", ["residual", "weight", "norm_out", "partial"])
+def test_scalar_load_width(H, offset, elems, field):
+    """The widest load (in BF16 elements) that H and every pointer's alignment allow."""
+    b = bufs(4, 64, H)
+    if offset:
+        if field == "partial":
+            b["partials"][2] += offset
+        else:
+            b[field] += offset
+    rc, p = plan(4, 64, H, **b)
+    assert rc == A.ARRMS_OK and p["variant"] == A.ARRMS_VARIANT_SCALAR
+    assert p["elems_per_load"] == elems and p["vec_per_thread"] == 0
+
+
+def test_scalar_load_width_tuning_and_vector_plans():
+    rc, p = plan(4, 64, 2044, tuning=A.arrms_tuning_t.make(scalar_elems=1))
+    assert p["elems_per_load"] == 1
+    rc, p = plan(4, 64, 5122, tuning=A.arrms_tuning_t.make(scalar_elems=4))   # capped by H
+    assert p["elems_per_load"] == 2
+    rc, p = plan(4, 64, 2048, variant=A.ARRMS_VARIANT_SCALAR)                # forced: widest allowed
+    assert p["elems_per_load"] == 4 and p["block"] == 256
+    rc, p = plan(4, 64, 2048)
+    assert p["variant"] == A.ARRMS_VARIANT_ROW and p["elems_per_load"] == 0
+    assert plan(4, 64, 2044, tuning=A.arrms_tuning_t.make(scalar_elems=3))[0] == A.ARRMS_ERR_INVALID_ARG
 
 
 def test_tuned_rows_per_block_keeps_one_vector_layout():

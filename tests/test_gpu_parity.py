@@ -97,7 +97,61 @@ SCALAR_SPANS = [(4, 5, 1, False), (3, 7, 3, False), (4, 9, 8191, False), (4, 9, 
 def test_scalar_spans(W, T, H, inplace):
     plan, _ = parity(W, T, H, variant=SCALAR, inplace=inplace, seed=H)
     assert plan["variant"] == SCALAR
-    assert plan["block"] == min(1024, -(-(-(-H // 8)) // 64) * 64)
+    assert plan["block"] == min(512 if W > 8 else 1024, -(-(-(-H // 8)) // 64) * 64)
+
+
+# The scalar variant loads 4, 2 or 1 BF16 elements at a time: the widest that H and
+# every pointer's alignment allow.  Each width, from H and from pointer offsets (on
+# every tensor, or on one tensor only), in one span and in several, at T = 1 and at
+# a prefill-sized T, with the rank count specialised and generic.
+SCALAR_WIDTHS = [
+    # W, T, H, byte offset, which tensors, load width
+    (4, 4096, 2044, 0, "all", 4), (4, 1, 2044, 0, "all", 4), (4, 4096, 5122, 0, "all", 2),
+    (4, 1, 5122, 0, "all", 2), (4, 4096, 2047, 0, "all", 1), (3, 300, 2046, 0, "all", 2),
+    (4, 4096, 2048, 8, "all", 4), (4, 130, 2048, 4, "all", 2), (4, 130, 2048, 2, "all", 1),
+    (4, 64, 2048, 8, "residual", 4), (4, 64, 2048, 4, "weight", 2), (4, 64, 2048, 2, "partial", 1),
+    (4, 64, 2044, 4, "norm_out", 2), (8, 33, 16388, 0, "all", 4), (8, 33, 16386, 0, "all", 2),
+    (2, 17, 24580, 8, "all", 4), (11, 29, 4092, 0, "all", 4), (16, 7, 6146, 4, "all", 2),
+    (1, 1000, 2044, 0, "all", 4), (1, 3, 1, 0, "all", 1),
+]
+
+
+def _shifted(t, off, dev):
+    """A copy of CPU tensor t on the GPU, starting `off` bytes past a 256-byte boundary."""
+    buf = torch.zeros(t.numel() + 16, dtype=torch.bfloat16, device=dev)
+    view = buf[off // 2:off // 2 + t.numel()].view(t.shape)
+    view.copy_(t.to(dev))
+    return view
+
+
+@pytest.mark.parametrize("W,T,H,off,which,elems", SCALAR_WIDTHS)
+def test_scalar_load_widths(W, T, H, off, which, elems):
+    where = "scalar width W=%d T=%d H=%d offset=%d on %s" % (W, T, H, off, which)
+    say("case " + where)
+    dev = torch.device("cuda", 0)
+    x, res, w = inputs(W, T, H, seed=H + off + W)
+    o_all = off if which == "all" else 0
+    xs = [_shifted(x[r], off if (which in ("all", "partial") and r == W - 1) or which == "all" else 0, dev)
+          for r in range(W)]
+    rs = _shifted(res, off if which in ("all", "residual") else 0, dev)
+    ws = _shifted(w, off if which in ("all", "weight") else 0, dev)
+    ro = _shifted(torch.zeros(T, H, dtype=torch.bfloat16), o_all, dev)
+    no = _shifted(torch.zeros(T, H, dtype=torch.bfloat16), off if which in ("all", "norm_out") else 0, dev)
+    o = op()
+    plan = o.plan(xs, rs, ws, 1e-6, ro, no)
+    assert plan["variant"] == SCALAR and plan["elems_per_load"] == elems, plan
+    o(xs, rs, ws, 1e-6, ro, no)
+    torch.cuda.synchronize()
+    n = assert_parity(synth.bits(ro.cpu()), synth.bits(no.cpu()), reference(x, res, w, 1e-6), where)
+    say("  plan %s, norm_out not bit-identical: %d of %d" % (plan, n, no.numel()))
+
+
+@pytest.mark.parametrize("elems", [1, 2, 4])
+@pytest.mark.parametrize("T,H", [(4096, 2048), (3, 16392), (5, 1000)])
+def test_scalar_tuned_narrower_loads(elems, T, H):
+    """Tuning caps the load width: the same rows through 2-, 4- and 8-byte loads."""
+    plan, _ = parity(4, T, H, variant=SCALAR, tuning=dict(scalar_elems=elems), seed=T + elems)
+    assert plan["elems_per_load"] == min(elems, 4 if H % 4 == 0 else (2 if H % 2 == 0 else 1))
 
 
 # The largest hidden size (ARRMS_MAX_HIDDEN) and the largest world size together,
