@@ -728,7 +728,7 @@ PMC_PASSES = {
 
 def pmc_command(workload: str, name: str) -> str:
     flag = "" if workload == "prefill" else " --workload %s" % workload
-    return ("timeout -s KILL 180 rocprofv3 --pmc %s --output-format csv -d gpurun_out/pmc_%s -o %s -- "
+    return ("timeout -s KILL 300 rocprofv3 --pmc %s --output-format csv -d gpurun_out/pmc_%s -o %s -- "
             "python -u bench.py%s --no-cpu --no-sweep --steps 50 --warmup 5"
             % (" ".join(PMC_PASSES[name]), name, name, flag))
 
@@ -795,7 +795,7 @@ def summarize_profiles(run_dir: str, workload: str, out_dir: str = None) -> None
         stalls = {"tcc_busy_cycles_sum": busy,
                   "read_dram_credit_stall_pct_of_busy": 100 * mean["TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum"] / busy,
                   "write_dram_credit_stall_pct_of_busy": 100 * mean["TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum"] / busy,
-                  "mean_read_requests_in_flight_per_busy_cycle": mean["TCC_EA0_RDREQ_LEVEL_sum"] / busy,
+                  "mean_read_requests_in_flight_per_channel": mean["TCC_EA0_RDREQ_LEVEL_sum"] / busy,
                   "mean_read_latency_cycles": mean["TCC_EA0_RDREQ_LEVEL_sum"] / mean["TCC_EA0_RDREQ_sum"]}
     commands = [pmc_command(workload, n) for n in PMC_PASSES]
     base = "%s_w%d_h%d_t%d" % (workload, W, H, T)
@@ -864,8 +864,8 @@ def summarize_profiles(run_dir: str, workload: str, out_dir: str = None) -> None
               stalls["read_dram_credit_stall_pct_of_busy"],
               "| write requests stalled on DRAM credits, %% of TCC busy cycles | %.2f |" %
               stalls["write_dram_credit_stall_pct_of_busy"],
-              "| mean read requests in flight per busy TCC cycle (summed over channels) | %.1f |" %
-              stalls["mean_read_requests_in_flight_per_busy_cycle"],
+              "| mean read requests in flight per TCC channel, over its busy cycles | %.1f |" %
+              stalls["mean_read_requests_in_flight_per_channel"],
               "| mean TCC-to-memory read latency, cycles | %.0f |" % stalls["mean_read_latency_cycles"]]
     with open(os.path.join(out_dir, "row_kernel_%s.md" % base), "w") as f:
         f.write("\n".join(L) + "\n")
