@@ -341,6 +341,43 @@ def copy_same_bytes(torch, nbytes, pairs=10, reps=200):
     return {"bytes_per_copy": 4 * n, "pairs": pairs, "us": ms * 1e3, "GB_s": 4 * n / (ms * 1e-3) / 1e9}
 
 
+def torch_streams(torch, nbytes=1 << 30, sets=4, reps=30):
+    """Same-box references from PyTorch's own kernels, each over `sets` rotating sets of
+    about `nbytes` of traffic per call (4 GiB in all, far beyond the 256 MB Infinity
+    Cache): a pure read (sum of a BF16 tensor into binary32), two reads and a write
+    (add), one read and a write (copy).  GB/s counts the bytes each must move."""
+    n = nbytes // 2  # BF16 elements per tensor
+    out = {}
+    a = torch.ones((sets, n), dtype=torch.bfloat16, device="cuda")
+    acc = torch.empty(sets, dtype=torch.float32, device="cuda")
+
+    def timed(fn, moved):
+        for i in range(2 * sets):
+            fn(i % sets)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(i % sets)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        return {"bytes": moved, "us": ms * 1e3, "GB_s": moved / (ms * 1e-3) / 1e9,
+                "frac_of_peak": moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    out["read_sum"] = timed(lambda i: torch.sum(a[i], dtype=torch.float32, out=acc[i]), 2 * n)
+    del acc
+    b = torch.ones((sets, n // 2), dtype=torch.bfloat16, device="cuda")
+    c = torch.empty((sets, n // 2), dtype=torch.bfloat16, device="cuda")
+    half = n // 2
+    out["add_2r1w"] = timed(lambda i: torch.add(a[i, :half], b[i], out=c[i]), 3 * 2 * half)
+    out["copy_1r1w"] = timed(lambda i: c[i].copy_(b[i]), 2 * 2 * half)
+    del a, b, c
+    torch.cuda.empty_cache()
+    for k, v in out.items():
+        log("torch %s: %.1f us, %.0f GB/s (%.1f%% of 8 TB/s)" % (k, v["us"], v["GB_s"], 100 * v["frac_of_peak"]))
+    return out
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -996,6 +1033,7 @@ def main():
     log("launch floor (one-element kernel, graph replay): %.2f us" % floor_us)
     copy = copy_context(torch, 512 * 2 ** 20)
     log("copy context: %.1f GB/s" % copy["GB_s"])
+    streams = torch_streams(torch) if not args.no_sweep else None
     copy_same = copy_same_bytes(torch, nbytes, pairs=max(2, min(10, int(4e9 // nbytes))))
     log("copy of the headline's byte count (%d B, rotating): %.2f us, %.1f GB/s" % (
         copy_same["bytes_per_copy"], copy_same["us"], copy_same["GB_s"]))
@@ -1044,6 +1082,7 @@ def main():
         "reduce_only": reduce_sweep,
         "copy_context": copy,
         "copy_same_bytes": copy_same,
+        "torch_streams": streams,
         "variants": variants,
         "scalar_widths": scalar,
         "splith_regime": splith_regime,
