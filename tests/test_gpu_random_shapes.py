@@ -1,6 +1,6 @@
 """Seeded random cases against the oracle: world sizes, token counts, hidden sizes
-(multiples of 8 and not), forced variants, tensors placed at 2-, 8- and 16-byte
-offsets (16-byte vector paths and the element-wise paths), in-place residual, and
+(multiples of 8 and not), forced variants, tensors placed at 2-, 4-, 8-, 12- and
+16-byte offsets (16-byte vector paths and every scalar load width), in-place residual, and
 the rank sum alone.  Every element is compared, to the parity bar of
 tests/gpu_util.py."""
 import os
@@ -28,11 +28,11 @@ def _cases(n, seed):
         H = int(rng.integers(1, 9000)) if rng.random() < 0.25 else 8 * int(rng.integers(1, 1025))
         # byte offset of each tensor from a 256-byte boundary (partials, residual, weight,
         # residual_out, norm_out): all 16-byte aligned in 70 % of the cases, else one or two
-        # tensors at a 2-, 8- or 18-byte offset
+        # tensors at a 2-, 4-, 8-, 12- or 18-byte offset (every load width of the scalar kernel)
         offs = [16 * int(rng.integers(0, 2)) for _ in range(W + 4)]
         if rng.random() >= 0.7:
             for k in rng.choice(W + 4, size=int(rng.integers(1, 3)), replace=False):
-                offs[int(k)] = int(rng.choice([2, 8, 18]))
+                offs[int(k)] = int(rng.choice([2, 4, 8, 12, 18]))
         inplace = bool(rng.random() < 0.25)
         if inplace:
             offs[W + 2] = offs[W]
