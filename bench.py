@@ -364,7 +364,7 @@ def torch_streams(torch, nbytes=1 << 30, sets=4, reps=30):
         ms = e0.elapsed_time(e1) / reps
         return {"bytes": moved, "us": ms * 1e3, "GB_s": moved / (ms * 1e-3) / 1e9,
                 "frac_of_peak": moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    out["read_sum"] = timed(lambda i: torch.sum(a[i], dtype=torch.float32, out=acc[i]), 2 * n)
+    out["read_sum"] = timed(lambda i: torch.sum(a[i], dim=0, dtype=torch.float32, out=acc[i]), 2 * n)
     del acc
     b = torch.ones((sets, n // 2), dtype=torch.bfloat16, device="cuda")
     c = torch.empty((sets, n // 2), dtype=torch.bfloat16, device="cuda")
