@@ -224,7 +224,8 @@ int arrms_plan_reduce(int cu_count, const arrms_tuning_t* tuning, int max_world,
  * The split-H workspace is a static device array of
  * ARRMS_NOALLOC_SCRATCH_DOUBLES doubles that each GPU holds from its first call
  * until the process ends; its address is looked up once per device, at that
- * device's first call.  A call whose plan is split-H and needs more than that,
+ * device's first call, which should therefore be made outside graph capture.
+ * Devices with an index of 64 or more are not served (ARRMS_ERR_HIP).  A call whose plan is split-H and needs more than that,
  * tokens * chunks_per_row doubles (see arrms_plan with ARRMS_MAX_WORLD, INT_MAX
  * tokens and ARRMS_MAX_HIDDEN as limits), returns ARRMS_ERR_SCRATCH and
  * enqueues nothing; other plans use no scratch.  Every call on one GPU shares

@@ -80,3 +80,53 @@ def test_reduce_in_graph():
         torch.cuda.synchronize()
         assert np.array_equal(synth.bits(out.cpu()), want)
     del g
+
+
+@pytest.mark.parametrize("W,T,H", [(8, 16, 8192), (4, 64, 2048), (3, 5, 1001)])
+def test_noalloc_in_graph(W, T, H):
+    """arrms_fused_noalloc captured in a graph (split-H with its static scratch, row, and
+    scalar plans): every replay, with eager work between replays, equals eager
+    arrms_fused bit for bit.  The first call on the device (its one-time set-up) is made
+    before capture."""
+    say("case graph noalloc W=%d T=%d H=%d" % (W, T, H))
+    o = op()
+    cases = [inputs(W, T, H, seed=420 + i) for i in range(3)]
+    xd = torch.empty((W, T, H), dtype=torch.bfloat16, device=DEV)
+    rd = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    wd = torch.empty((H,), dtype=torch.bfloat16, device=DEV)
+    outs = [(torch.empty_like(rd), torch.empty_like(rd)) for _ in range(2)]
+    xd.copy_(cases[0][0].to(DEV)); rd.copy_(cases[0][1].to(DEV)); wd.copy_(cases[0][2].to(DEV))
+
+    def call(k, stream):
+        ro, no = outs[k]
+        rc = A.arrms_fused_noalloc([xd[r].data_ptr() for r in range(W)], W, T, H, rd.data_ptr(), wd.data_ptr(),
+                                   1e-6, ro.data_ptr(), no.data_ptr(), stream)
+        assert rc == A.ARRMS_OK, A.arrms_status_string(rc)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(0, side.cuda_stream)   # warm-up and one-time set-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        s = torch.cuda.current_stream().cuda_stream
+        call(0, s)
+        call(1, s)   # a second call in the same replay reuses the scratch
+    for rep in range(6):
+        x, r, w = cases[rep % 3]
+        xd.copy_(x.to(DEV)); rd.copy_(r.to(DEV)); wd.copy_(w.to(DEV))
+        for ro, no in outs:
+            ro.fill_(0); no.fill_(0)   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eager_ro, eager_no = o(xd, rd, wd, 1e-6)
+        torch.cuda.synchronize()
+        want_ro, want_no = synth.bits(eager_ro.cpu()), synth.bits(eager_no.cpu())
+        for ro, no in outs:
+            assert np.array_equal(synth.bits(ro.cpu()), want_ro)
+            assert np.array_equal(synth.bits(no.cpu()), want_no)
+        assert_parity(want_ro, want_no, reference(x, r, w, 1e-6), "graph noalloc replay %d" % rep)
+    del g

@@ -1,8 +1,9 @@
 """Performance floors that catch regressions (a lost streaming hint, a spilling
 kernel, a bad plan), with wide margins so that box-to-box variance cannot trip
 them: the prefill shape (W=4 T=4096 H=2048) must stream at >= 4.5 TB/s (it runs
-at about 5.6 TB/s on MI355X) and a decode call (T=1) must take < 8 us of GPU time
-per back-to-back call (about 2.6-3.8 us)."""
+at about 5.6 TB/s on MI355X), the same rows with H = 2044 (the scalar variant, 8-byte
+loads) at >= 4.0 TB/s (about 5.3 TB/s), and a decode call (T=1) must take < 8 us of
+GPU time per back-to-back call (about 2.6-3.8 us)."""
 
 import pytest
 import torch
@@ -28,9 +29,10 @@ def _gpu_us_per_call(fn, calls):
     return e0.elapsed_time(e1) * 1e3 / calls
 
 
-@pytest.mark.parametrize("T,floor_gbs,ceil_us", [(4096, 4500.0, None), (1, None, 8.0)])
-def test_performance_floor(T, floor_gbs, ceil_us):
-    W, H = 4, 2048
+@pytest.mark.parametrize("T,H,floor_gbs,ceil_us", [(4096, 2048, 4500.0, None), (4096, 2044, 4000.0, None),
+                                                    (1, 2048, None, 8.0)])
+def test_performance_floor(T, H, floor_gbs, ceil_us):
+    W = 4
     sets = 4 if T > 1 else 1  # 4 x 117 MB rotate past the 256 MB Infinity Cache
     bufs = []
     for i in range(sets):
@@ -40,6 +42,8 @@ def test_performance_floor(T, floor_gbs, ceil_us):
     w = torch.rand(H, device=DEV).bfloat16() + 0.5
     with A.FusedReduceResidualRMSNorm(max_world=W, max_tokens=T, max_hidden=H, device=0) as op:
         calls = [op.bind(x, r, w, 1e-6, ro, no) for x, r, ro, no in bufs]
+        plan = op.plan(bufs[0][0], bufs[0][1], w, 1e-6, bufs[0][2], bufs[0][3])
+        assert plan["variant"] == (A.ARRMS_VARIANT_ROW if H % 8 == 0 else A.ARRMS_VARIANT_SCALAR)
         state = {"i": 0}
 
         def step():
