@@ -237,8 +237,10 @@ def time_isolated(torch, call, K):
     return out
 
 
-def time_graph(torch, call, calls_per_graph, replays):
-    """calls_per_graph calls captured in one HIP graph, replayed; ms per call."""
+def time_graph(torch, call, calls_per_graph, replays, flush=None):
+    """calls_per_graph calls captured in one HIP graph, replayed; ms per call.  With
+    `flush`, it runs before every replay, outside the timed interval of that replay
+    (events around each replay), so that no replay finds its data in the caches."""
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -257,6 +259,18 @@ def time_graph(torch, call, calls_per_graph, replays):
     call.stream = saved
     g.replay()
     torch.cuda.synchronize()
+    if flush is not None:
+        total = 0.0
+        for _ in range(replays):
+            flush()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            total += e0.elapsed_time(e1)
+        del g
+        return total / (replays * calls_per_graph)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(replays):
@@ -461,6 +475,13 @@ class Ctx:
         return Caller(self.A, self.op.handle, self.pool.sets(t), self.W, t, self.H, self.pool.weight.data_ptr(),
                       self.eps, self.stream)
 
+    def flush(self):
+        """Stream 1 GiB through memory that no call uses (a 512 MiB device copy), so that the
+        256 MB Infinity Cache holds none of the pool's data afterwards."""
+        if not hasattr(self, "_flush_buf"):
+            self._flush_buf = self.torch.empty((2, 256 * 2 ** 20), dtype=self.torch.bfloat16, device="cuda")
+        self._flush_buf[1].copy_(self._flush_buf[0])
+
     def plan(self, t):
         s, W = self.pool.slot, self.W
         return self.op.plan(s[0, :W, :t], s[0, W, :t], self.pool.weight, self.eps, s[0, W + 1, :t], s[0, W + 2, :t])
@@ -470,7 +491,10 @@ VARIANT_NAMES = {1: "row", 2: "splith", 3: "scalar"}
 
 
 def sweep_tokens(ctx):
-    """Sweep over T: back-to-back, per-launch, isolated and graph replay."""
+    """Sweep over T: back-to-back, per-launch, isolated and graph replay with data coming
+    from HBM (each leg starts after a cache flush and its calls take distinct buffers, the
+    graph's 100 calls too, with a flush before every replay), then back-to-back and graph
+    replay on one set of buffers repeated (hot: inputs in the caches)."""
     torch, W, H = ctx.torch, ctx.W, ctx.H
     sweep = []
     for t in SWEEP_T:
@@ -479,10 +503,13 @@ def sweep_tokens(ctx):
         for _ in range(100):
             c()
         k = 2000 if t <= 1024 else 1000
+        ctx.flush()
         wall, gpu = time_back_to_back(torch, c, k)
+        ctx.flush()
         d = time_per_launch(torch, c, 300)
+        ctx.flush()
         iso = time_isolated(torch, c, 100)
-        gr = time_graph(torch, c, 100, 10)
+        gr = time_graph(torch, c, 100, 10, flush=ctx.flush)
         # the same call repeated on one set of buffers (inputs and outputs stay in the caches)
         hot = Caller(ctx.A, ctx.op.handle, ctx.pool.sets(t)[:1], W, t, H, ctx.pool.weight.data_ptr(), ctx.eps,
                      ctx.stream)
