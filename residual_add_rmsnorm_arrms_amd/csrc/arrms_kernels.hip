@@ -201,16 +201,16 @@ __global__ void __launch_bounds__(1024) splith_norm_kernel(const SplitNormArgs a
 // aligned).  Loads are E BF16 elements wide (E = 4, 2 or 1: 8-, 4- or 2-byte
 // loads), the widest that H and the alignment of every pointer allow.  One row per
 // workgroup of n lanes (n <= 1024, or 512 for more than 8 ranks), XCD runs as in
-// the row variant.  The row is
-// walked in spans of kScalarSpan * n elements; in a span lane l owns the E-element
-// groups l, l + n, ..., l + (8 / E - 1) * n, so each load instruction of a wave
-// covers 128 * E contiguous bytes and a lane moves 16 bytes per input per span,
-// as in the row variant.  Group indexes past the row are clamped for loads (which
-// then stay inside the row, in one basic block, so the compiler issues the span's
-// loads of every rank together) and masked for stores and for the sum of squares.
-// When the row fits one span, residual_out stays in registers for the second pass;
+// the row variant.  The row is walked in spans of kScalarSpan * n elements; in a
+// span lane l owns the E-element groups l, l + n, ..., l + (8 / E - 1) * n, so each
+// load instruction of a wave covers 128 * E contiguous bytes and a lane moves 16
+// bytes per input per span, as in the row variant.  Group indexes past the row are
+// clamped for loads (which then stay inside the row, in one basic block, so the
+// compiler issues the span's loads of every rank together) and masked for stores
+// and for the sum of squares; what a clamped load returns is never used.  When the
+// row fits one span, residual_out stays in registers for the second pass;
 // otherwise the second pass re-reads it (each group is read back by the lane that
-// stored it, after the barrier).
+// stored it).
 constexpr int kScalarSpan = 8;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
