@@ -792,7 +792,7 @@ PMC_PASSES = {
 
 def pmc_command(workload: str, name: str) -> str:
     flag = "" if workload == "prefill" else " --workload %s" % workload
-    return ("timeout -s KILL 300 rocprofv3 --pmc %s --output-format csv -d gpurun_out/pmc_%s -o %s -- "
+    return ("timeout -s KILL 300 rocprofv3 --pmc %s --output-format csv -d <run dir>/pmc_%s -o %s -- "
             "python -u bench.py%s --no-cpu --no-sweep --steps 50 --warmup 5"
             % (" ".join(PMC_PASSES[name]), name, name, flag))
 
@@ -876,7 +876,7 @@ def summarize_profiles(run_dir: str, workload: str, out_dir: str = None) -> None
     out_dir = out_dir or os.path.join(ROOT, "profiles")
     json.dump(traffic, open(os.path.join(out_dir, os.path.basename(traffic_file(wl))), "w"), indent=1)
     cmd_trace = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
-                 "-d gpurun_out/prof_bench -o bench -- python -u bench.py" + flag)
+                 "-d <run dir>/prof_bench -o bench -- python -u bench.py" + flag)
     L = ["# %s on W=%d T=%d H=%d (%s) — rocprofv3 summary\n" % (kname, W, T, H, workload),
          "GPU: MI355X (gfx950), one GPU.  Source hash of the kernels, planner and argument packing (sha256[:16] "
          "of the code without comments, as bench.py computes it) = `%s`.  Written by `python bench.py --summarize "
