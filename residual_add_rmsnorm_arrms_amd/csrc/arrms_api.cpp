@@ -232,9 +232,14 @@ int plan_splith(int cu_count, int max_hidden, int world, int tokens, int hidden,
 // ranks: the kernels' __launch_bounds__).  Loads are `elems` BF16
 // elements wide (the widest that H and every pointer's alignment allow, at most
 // the tuned width).  XCD runs as in the row variant (about 3 MiB of traffic per run).
-void plan_scalar(int world, int tokens, int hidden, int elems, const arrms_tuning_t* t, arrms_plan_t* p) {
+// Unless every row of the first partial starts on a 128-byte line, the kernel
+// shifts its lanes by up to 63 elements to cover whole lines; the span leaves
+// room for that shift.
+void plan_scalar(int world, int tokens, int hidden, int elems, const void* first_partial, const arrms_tuning_t* t,
+                 arrms_plan_t* p) {
     const int max_block = world > 8 ? 512 : 1024;
-    int block = ((hidden + 7) / 8 + 63) / 64 * 64;
+    const bool lines = (reinterpret_cast<uintptr_t>(first_partial) & 127u) == 0 && hidden % 64 == 0;
+    int block = ((hidden + (lines ? 0 : 63) + 7) / 8 + 63) / 64 * 64;
     if (block > max_block) block = max_block;
     if (t && t->scalar_elems && t->scalar_elems < elems) elems = t->scalar_elems;
     p->variant = ARRMS_VARIANT_SCALAR;
@@ -352,7 +357,7 @@ int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
     const int elems = scalar_elems(hidden, any);
     switch (variant) {
         case ARRMS_VARIANT_SCALAR:
-            plan_scalar(world, tokens, hidden, elems, tuning, plan);
+            plan_scalar(world, tokens, hidden, elems, partials[0], tuning, plan);
             return ARRMS_OK;
         case ARRMS_VARIANT_ROW:
             if (!vector_ok || hidden > ARRMS_ROW_MAX_HIDDEN) return ARRMS_ERR_UNSUPPORTED;
@@ -364,7 +369,7 @@ int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
             break;
     }
     if (!vector_ok) {
-        plan_scalar(world, tokens, hidden, elems, tuning, plan);
+        plan_scalar(world, tokens, hidden, elems, partials[0], tuning, plan);
         return ARRMS_OK;
     }
     int split_max = (tuning && tuning->splith_max_tokens >= 0) ? tuning->splith_max_tokens
@@ -381,7 +386,7 @@ int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
     memset(plan, 0, sizeof *plan);
     if (plan_splith(cu_count, max_hidden, world, tokens, hidden, tuning, plan) == ARRMS_OK) return ARRMS_OK;
     memset(plan, 0, sizeof *plan);
-    plan_scalar(world, tokens, hidden, elems, tuning, plan);
+    plan_scalar(world, tokens, hidden, elems, partials[0], tuning, plan);
     return ARRMS_OK;
 }
 

@@ -211,6 +211,13 @@ __global__ void __launch_bounds__(1024) splith_norm_kernel(const SplitNormArgs a
 // row fits one span, residual_out stays in registers for the second pass;
 // otherwise the second pass re-reads it (each group is read back by the lane that
 // stored it).
+// A row whose start is not on a 128-byte line (odd H, or a pointer offset) would
+// make every wave instruction straddle two lines.  So the lanes' group indexes are
+// shifted back by the row's offset within its line of the first partial: index i
+// takes group i - shift, the wave instructions then cover whole lines of every
+// tensor that is aligned like that partial, and indexes before the row start are
+// clamped and masked like those past its end.  The shift is dropped where it would
+// push a row that fits one span into a second.
 constexpr int kScalarSpan = 8;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -261,6 +268,10 @@ __global__ void __launch_bounds__(scalar_max_threads<W>()) scalar_kernel(const S
     const int ng = H / E;  // groups per row
     const int span = S * n;
     const size_t base = static_cast<size_t>(row) * static_cast<size_t>(ng);
+    const int line_off = static_cast<int>(
+        (reinterpret_cast<uintptr_t>(static_cast<const G*>(a.x.p[0]) + base) & 127u) / sizeof(G));
+    const int shift = (ng <= span && ng + line_off > span) ? 0 : line_off;
+    const int nidx = ng + shift;  // lane indexes that cover the row
     const G* res = static_cast<const G*>(a.residual) + base;
     const G* w = static_cast<const G*>(a.weight);
     G* ro_out = static_cast<G*>(a.residual_out) + base;
@@ -273,18 +284,21 @@ __global__ void __launch_bounds__(scalar_max_threads<W>()) scalar_kernel(const S
     // the generic kernel (up to 16 ranks, W known at run time) adds the ranks after
     // x_0 one at a time instead, which keeps its registers within budget.
     constexpr int WL = W > 0 ? W : 1;
-    for (int g0 = 0; g0 < ng; g0 += span) {
+    for (int i0 = 0; i0 < nidx; i0 += span) {
+        const int g0 = i0 - shift;  // group of the span's first index
         // every load of the span first (the ranks kept, residual, weight), then the arithmetic
         G xv[WL][S];
         G rs[S];
 #pragma unroll
         for (int u = 0; u < S; ++u) {
-            const int g = min(g0 + u * n + tid, ng - 1);
+            const int g = min(max(g0 + u * n + tid, 0), ng - 1);
 #pragma unroll
             for (int r = 0; r < WL; ++r) xv[r][u] = __builtin_nontemporal_load(static_cast<const G*>(a.x.p[r]) + base + g);
             rs[u] = __builtin_nontemporal_load(res + g);
             wk[u] = w[g];
         }
+        // keep the scheduler from interleaving the arithmetic (and its waits) into the loads
+        __builtin_amdgcn_sched_barrier(0);
         // binary32 rank sums, rank order 0, 1, ..., W-1 for every element
         float acc[S][E];
 #pragma unroll
@@ -301,7 +315,7 @@ __global__ void __launch_bounds__(scalar_max_threads<W>()) scalar_kernel(const S
                 const G* xr = static_cast<const G*>(a.x.p[r]) + base;
                 G v[S];
 #pragma unroll
-                for (int u = 0; u < S; ++u) v[u] = __builtin_nontemporal_load(xr + min(g0 + u * n + tid, ng - 1));
+                for (int u = 0; u < S; ++u) v[u] = __builtin_nontemporal_load(xr + min(max(g0 + u * n + tid, 0), ng - 1));
 #pragma unroll
                 for (int u = 0; u < S; ++u)
 #pragma unroll
@@ -317,7 +331,7 @@ __global__ void __launch_bounds__(scalar_max_threads<W>()) scalar_kernel(const S
             for (int k = 0; k < E; ++k) o[k] = Group<E>::get(rg, k) + Group<E>::get(rs[u], k);
             const G og = pack<E>(o);
             keep[u] = og;
-            if (g < ng) {
+            if (g >= 0 && g < ng) {
                 ro_out[g] = og;
 #pragma unroll
                 for (int k = 0; k < E; ++k) {
@@ -335,22 +349,23 @@ __global__ void __launch_bounds__(scalar_max_threads<W>()) scalar_kernel(const S
     for (int i = 1; i < (n >> 6); ++i) total = total + wave_ss[i];
     const float inv = inv_rms(total, static_cast<double>(H), a.eps);
 
-    if (ng <= span) {
+    if (nidx <= span) {
 #pragma unroll
         for (int u = 0; u < S; ++u) {
-            const int g = u * n + tid;
+            const int g = u * n + tid - shift;
             float v[E];
 #pragma unroll
             for (int k = 0; k < E; ++k) v[k] = (Group<E>::get(keep[u], k) * inv) * Group<E>::get(wk[u], k);
-            if (g < ng) __builtin_nontemporal_store(pack<E>(v), n_out + g);
+            if (g >= 0 && g < ng) __builtin_nontemporal_store(pack<E>(v), n_out + g);
         }
         return;
     }
-    for (int g0 = 0; g0 < ng; g0 += span) {
+    for (int i0 = 0; i0 < nidx; i0 += span) {
+        const int g0 = i0 - shift;
         G rv[S], wv[S];
 #pragma unroll
         for (int u = 0; u < S; ++u) {
-            const int g = min(g0 + u * n + tid, ng - 1);
+            const int g = min(max(g0 + u * n + tid, 0), ng - 1);
             rv[u] = ro_out[g];
             wv[u] = w[g];
         }
@@ -360,7 +375,7 @@ __global__ void __launch_bounds__(scalar_max_threads<W>()) scalar_kernel(const S
             float v[E];
 #pragma unroll
             for (int k = 0; k < E; ++k) v[k] = (Group<E>::get(rv[u], k) * inv) * Group<E>::get(wv[u], k);
-            if (g < ng) __builtin_nontemporal_store(pack<E>(v), n_out + g);
+            if (g >= 0 && g < ng) __builtin_nontemporal_store(pack<E>(v), n_out + g);
         }
     }
 }
