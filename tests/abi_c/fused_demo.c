@@ -1,7 +1,9 @@
 /* The whole boundary from plain C on the GPU, without Python or torch:
  * arrms_create -> arrms_fused -> arrms_destroy on device buffers allocated with
  * hipMalloc, the outputs checked against the CPU oracle (liboracle.so, test
- * infrastructure), then a C loop of back-to-back calls timed with HIP events.
+ * infrastructure), then a C loop of back-to-back calls timed with HIP events;
+ * then the no-allocation entry point on the same inputs, whose outputs must equal
+ * arrms_fused's bit for bit, and its own timed loop.
  *
  * usage: fused_demo W T H [timed_calls]
  * Inputs: seeded normals / uniforms from libsynth.so, cut to BF16 by keeping the
@@ -165,6 +167,41 @@ int main(int argc, char** argv) {
     printf("timing: W=%d T=%d H=%d, %d back-to-back calls from C (same buffers): %.2f us/call, %.1f GB/s\n", W, T,
            H, calls, us, bytes / (us * 1e-6) / 1e9);
 
+    /* the no-allocation entry point (current device, no handle): same bits as arrms_fused */
+    HIP_OK(hipMemset(dro, 0, n * 2));
+    HIP_OK(hipMemset(dno, 0, n * 2));
+    HIP_OK(hipDeviceSynchronize());
+    rc = arrms_fused_noalloc((const void* const*)dx, W, T, H, dres, dw, eps, dro, dno, NULL);
+    if (rc != ARRMS_OK) {
+        printf("FAIL arrms_fused_noalloc: %s\n", arrms_status_string(rc));
+        return 1;
+    }
+    HIP_OK(hipDeviceSynchronize());
+    uint16_t* ro2 = (uint16_t*)malloc(n * 2);
+    uint16_t* no2 = (uint16_t*)malloc(n * 2);
+    if (!ro2 || !no2) {
+        printf("FAIL host allocation\n");
+        return 1;
+    }
+    HIP_OK(hipMemcpy(ro2, dro, n * 2, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(no2, dno, n * 2, hipMemcpyDeviceToHost));
+    const int same = memcmp(ro2, ro, n * 2) == 0 && memcmp(no2, no, n * 2) == 0;
+    printf("%s arrms_fused_noalloc outputs %s arrms_fused's\n", same ? "ok  " : "FAIL",
+           same ? "bit-identical to" : "differ from");
+    free(ro2), free(no2);
+    HIP_OK(hipEventRecord(e0, NULL));
+    for (k = 0; k < calls; ++k) {
+        rc = arrms_fused_noalloc((const void* const*)dx, W, T, H, dres, dw, eps, dro, dno, NULL);
+        if (rc != ARRMS_OK) {
+            printf("FAIL arrms_fused_noalloc in the timed loop: %s\n", arrms_status_string(rc));
+            return 1;
+        }
+    }
+    HIP_OK(hipEventRecord(e1, NULL));
+    HIP_OK(hipEventSynchronize(e1));
+    HIP_OK(hipEventElapsedTime(&ms, e0, e1));
+    printf("timing: arrms_fused_noalloc, %d back-to-back calls from C: %.2f us/call\n", calls, 1e3 * ms / calls);
+
     HIP_OK(hipEventDestroy(e0));
     HIP_OK(hipEventDestroy(e1));
     rc = arrms_destroy(h);
@@ -174,5 +211,5 @@ int main(int argc, char** argv) {
     HIP_OK(hipFree(dro));
     HIP_OK(hipFree(dno));
     free(f), free(hx), free(hres), free(hw), free(ro), free(no), free(ref_ro), free(ref_no);
-    return (pass && rc == ARRMS_OK) ? 0 : 1;
+    return (pass && same && rc == ARRMS_OK) ? 0 : 1;
 }

@@ -1,7 +1,8 @@
 """The boundary from plain C on the GPU (tests/abi_c/fused_demo.c, built by
 __graft_entry__.build()): create, fused call on hipMalloc'd buffers, destroy, with the
 outputs checked against the oracle inside the C program, then a C loop of
-back-to-back calls timed with HIP events (printed)."""
+back-to-back calls timed with HIP events (printed); then the no-allocation entry
+point, which must give arrms_fused's bits, and its own timed loop."""
 import os
 import subprocess
 
@@ -26,4 +27,4 @@ def test_c_program_end_to_end(W, T, H, calls):
     out = res.stdout + res.stderr
     say(out.strip())
     assert res.returncode == 0, out
-    assert "FAIL" not in out and "timing:" in out
+    assert "FAIL" not in out and "timing:" in out and "arrms_fused_noalloc outputs bit-identical" in out
