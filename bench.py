@@ -470,6 +470,7 @@ class Ctx:
     def __init__(self, torch, A, synth, op, pool, W, H, eps, stream):
         self.torch, self.A, self.synth, self.op, self.pool = torch, A, synth, op, pool
         self.W, self.H, self.eps, self.stream = W, H, eps, stream
+        self.cu = torch.cuda.get_device_properties(0).multi_processor_count
 
     def caller(self, t):
         return Caller(self.A, self.op.handle, self.pool.sets(t), self.W, t, self.H, self.pool.weight.data_ptr(),
@@ -625,6 +626,48 @@ def forced_variants(ctx):
                 name, t, g * 1e3, b / (g * 1e-3) / 1e9, p["grid"], p["block"], p["kernels"]))
     op.set_variant(A.ARRMS_VARIANT_AUTO)
     return variants
+
+
+def reduce_offsets(ctx, W=4, T=4096):
+    """The rank sum alone at W=4 T=4096 H=2048 with its tensors placed at byte offsets:
+    every tensor at the same offset (16-byte loads after a short head) and the output
+    at an offset the partials do not share (8-, 4- and 2-byte loads).  Back-to-back GPU
+    time over the prefill pool's buffers: a call reads rows of partials 0..W-1 of a slot,
+    so an offset read ends at most 14 bytes into the next tensor of the same slot."""
+    torch, A, op, pool, H = ctx.torch, ctx.A, ctx.op, ctx.pool, ctx.H
+    fn = A.load().arrms_reduce
+    vp = ctypes.c_void_p
+    te = pool.tensor_elems * 2
+    # one spare row per output slot: an offset output still ends inside its slot
+    out = torch.empty((pool.slots, pool.T + 1, H), dtype=torch.bfloat16, device="cuda")
+    res = []
+    for part_off, out_off in ((0, 0), (2, 2), (0, 8), (0, 4), (0, 2)):
+        calls = []
+        for j in range(pool.T // T):
+            for sl in range(pool.slots):
+                base = pool.base + sl * (pool.W + 3) * te + j * T * H * 2
+                parts = [base + r * te + part_off for r in range(W)]
+                o = out[sl].data_ptr() + j * T * H * 2 + out_off
+                calls.append(((vp * W)(*parts), vp(o)))
+        rc, p = A.arrms_plan_reduce(ctx.cu, None, 16, pool.T, H, [c for c in calls[0][0]], W, T, H, calls[0][1].value)
+        state = {"i": 0}
+
+        def call():
+            a = calls[state["i"] % len(calls)]
+            state["i"] += 1
+            r = fn(vp(op.handle), a[0], W, T, H, a[1], vp(ctx.stream))
+            if r:
+                raise RuntimeError("arrms_reduce returned %d" % r)
+        for _ in range(20):
+            call()
+        _, ms = time_back_to_back(torch, call, 300)
+        b = 2 * T * H * (W + 1)
+        res.append({"W": W, "T": T, "H": H, "partials_offset": part_off, "reduced_offset": out_off,
+                    "elems_per_load": p["elems_per_load"], "us": ms * 1e3, "GB_s": b / (ms * 1e-3) / 1e9})
+        log("rank sum W=%d T=%d, partials +%d B, output +%d B: %d-byte loads, %.2f us, %.0f GB/s" % (
+            W, T, part_off, out_off, 2 * p["elems_per_load"], ms * 1e3, b / (ms * 1e-3) / 1e9))
+    del out
+    return res
 
 
 def scalar_widths(ctx, T=4096):
@@ -1044,7 +1087,7 @@ def main():
         log("parity of the timed configuration vs oracle: %s" % parity)
 
     sweep, fit, fusion, reduce_sweep, variants, splith_regime, worlds = [], None, None, [], [], [], []
-    ceiling, scalar = None, []
+    ceiling, scalar, reduce_offs = None, [], []
     if not args.no_sweep:
         ctx = Ctx(torch, A, synth, op, pool, W, H, eps, stream)
         ceiling = read_ceiling(ctx, achieved)
@@ -1053,6 +1096,7 @@ def main():
         fusion, reduce_sweep = fusion_and_rank_sum(ctx, T, nbytes, gpu_ms)
         variants = forced_variants(ctx)
         scalar = scalar_widths(ctx)
+        reduce_offs = reduce_offsets(ctx)
         splith_regime = splith_crossover(ctx)
         worlds = world_sweep(ctx)
 
@@ -1112,6 +1156,7 @@ def main():
         "torch_streams": streams,
         "variants": variants,
         "scalar_widths": scalar,
+        "reduce_offsets": reduce_offs,
         "splith_regime": splith_regime,
         "world_sweep": worlds,
         "ceiling": ceiling,

@@ -59,7 +59,7 @@ extern "C" {
 #define ARRMS_VARIANT_SCALAR 3 /* 8-, 4- or 2-byte loads: any H, any 2-byte alignment */
 /* Plan kinds of arrms_reduce (the rank sum alone). */
 #define ARRMS_VARIANT_REDUCE 4        /* 16-byte vector loads, flat over T*H elements */
-#define ARRMS_VARIANT_REDUCE_SCALAR 5 /* element-wise, any 2-byte alignment */
+#define ARRMS_VARIANT_REDUCE_SCALAR 5 /* 8-, 4- or 2-byte loads: pointers at different offsets modulo 16 */
 
 #define ARRMS_MAX_WORLD 16        /* largest W */
 #define ARRMS_MAX_HIDDEN 65536    /* largest H */
@@ -80,7 +80,8 @@ typedef struct {
     int kernels;         /* kernel launches per call: 2 for split-H, else 1 (0: none) */
     int blocks;          /* logical workgroups per kernel (grid minus padding of the XCD mapping) */
     int xcd_chunk;       /* K > 0: runs of K consecutive workgroups (rows) kept on one XCD; 0: hardware order */
-    int elems_per_load;  /* scalar: BF16 elements per load (4, 2 or 1: 8-, 4- or 2-byte loads); else 0 */
+    int elems_per_load;  /* scalar: BF16 elements per load (4, 2 or 1: 8-, 4- or 2-byte loads); rank sum: 8, 4,
+                            2 or 1; else 0 */
 } arrms_plan_t;
 
 /* Optional tuning overrides; 0 (or -1 where stated) keeps the automatic choice.
@@ -92,7 +93,7 @@ typedef struct {
     int splith_max_tokens; /* automatic variant uses split-H when tokens <= this; -1 automatic */
     int xcd_chunk;         /* -1 automatic; 0 hardware round-robin; K > 0 runs of K blocks per XCD */
     int rows_per_block;    /* row: token rows per workgroup (power of two); 0 automatic */
-    int scalar_elems;      /* scalar: at most this many BF16 elements per load (1, 2 or 4); 0 automatic */
+    int scalar_elems;      /* scalar and rank sum: at most this many BF16 elements per load (1, 2 or 4); 0 automatic */
 } arrms_tuning_t;
 
 /*
@@ -201,9 +202,11 @@ int arrms_query_plan(arrms_handle_t h, const void* const* partials, int world, i
  *   partials : HOST array of `world` device pointers, each BF16 [tokens][hidden]
  *   reduced  : BF16 [tokens][hidden] output; may be exactly one of the partials,
  *              may not otherwise overlap them
- * Limits, 2-byte alignment, asynchrony and error behaviour as for arrms_fused;
- * every pointer 16-byte aligned selects the vector kernel (any T*H), else the
- * element-wise kernel.  Uses no workspace.
+ * Limits, 2-byte alignment, asynchrony and error behaviour as for arrms_fused.
+ * The sum is flat over the T*H elements, so only the pointers' offsets matter:
+ * loads are 16 bytes wide when every pointer has the same offset modulo 16 (the
+ * few elements before the first aligned one are summed one by one), else 8, 4 or
+ * 2 bytes wide, the widest at which the offsets agree.  Uses no workspace.
  */
 int arrms_reduce(arrms_handle_t h, const void* const* partials, int world, int tokens, int hidden,
                  void* reduced, hipStream_t stream);

@@ -420,32 +420,35 @@ int plan_reduce(int cu_count, const arrms_tuning_t* tuning, int max_world, int m
     plan->chunks_per_row = 1;
     plan->block = 256;
     plan->threads_per_row = 256;
-    if (any & 15u) {
-        const long long want = (count + 255) / 256;
-        const long long cap = 8LL * cu_count;
-        plan->variant = ARRMS_VARIANT_REDUCE_SCALAR;
-        plan->blocks = static_cast<int>(want < cap ? want : cap);
-        plan->grid = plan->blocks;
-        return ARRMS_OK;
+    // Load width: the widest at which every pointer has the same offset (the first
+    // few elements up to the aligned start are summed element-wise); tuning may cap it.
+    int elems = 8, head = 0;
+    arrms::reduce_alignment(partials, world, reduced, count, (tuning && tuning->scalar_elems) ? tuning->scalar_elems : 8,
+                            &elems, &head);
+    int vpt = 1;
+    if (elems == 8) {
+        vpt = kReduceAutoVpt;
+        if (tuning && tuning->vec_per_thread) vpt = tuning->vec_per_thread;
+        if (world > 8) {
+            if (tuning && tuning->vec_per_thread > 1) return ARRMS_ERR_UNSUPPORTED;
+            vpt = 1;
+        }
+        if (vpt > 4) return ARRMS_ERR_UNSUPPORTED;
     }
-    int vpt = kReduceAutoVpt;
-    if (tuning && tuning->vec_per_thread) vpt = tuning->vec_per_thread;
-    if (world > 8) {
-        if (tuning && tuning->vec_per_thread > 1) return ARRMS_ERR_UNSUPPORTED;
-        vpt = 1;
-    }
-    if (vpt > 4) return ARRMS_ERR_UNSUPPORTED;
-    const long long nvec = count / 8;
-    const long long per_block = 256LL * vpt;
-    long long blocks = (nvec + per_block - 1) / per_block;
+    // lanes move 16 bytes per partial per step whatever the width: groups per lane
+    const int groups_per_lane = elems == 8 ? vpt : 8 / elems;
+    const long long ngroups = (count - head) / elems;
+    const long long per_block = 256LL * groups_per_lane;
+    long long blocks = (ngroups + per_block - 1) / per_block;
     if (blocks < 1) blocks = 1;
     if (blocks > 0x7ffffff0LL) return ARRMS_ERR_UNSUPPORTED;
-    plan->variant = ARRMS_VARIANT_REDUCE;
-    plan->vec_per_thread = vpt;
+    plan->variant = elems == 8 ? ARRMS_VARIANT_REDUCE : ARRMS_VARIANT_REDUCE_SCALAR;
+    plan->vec_per_thread = elems == 8 ? vpt : 0;
+    plan->elems_per_load = elems;
     plan->blocks = static_cast<int>(blocks);
     int k = 0;
     if (plan->blocks >= 64) {
-        const long block_bytes = 16L * per_block * (world + 1);
+        const long block_bytes = 2L * elems * per_block * (world + 1);
         k = 1;
         while (2L * k * block_bytes <= kXcdRunBytes) k *= 2;
     }
@@ -517,14 +520,20 @@ int arrms_reduce(arrms_handle_t h, const void* const* partials, int world, int t
     const int rc = arrms_plan_reduce(h->cu_count, h->has_tuning ? &h->tuning : nullptr, h->max_world, h->max_tokens,
                                      h->max_hidden, partials, world, tokens, hidden, reduced, &p);
     if (rc != ARRMS_OK || p.grid == 0) return rc;
+    // the pointers advanced to their first element aligned for the planned load width
+    const long long count = static_cast<long long>(tokens) * hidden;
+    int elems = 0, head = 0;
+    arrms::reduce_alignment(partials, world, reduced, count, p.elems_per_load, &elems, &head);
     arrms::Args a;
     memset(&a, 0, sizeof a);
-    for (int r = 0; r < world; ++r) a.x.p[r] = partials[r];
-    a.reduced = reduced;
+    for (int r = 0; r < world; ++r) a.x.p[r] = static_cast<const uint16_t*>(partials[r]) + head;
+    a.reduced = static_cast<uint16_t*>(reduced) + head;
     a.world = world;
     a.tokens = tokens;
     a.hidden = hidden;
-    a.count = static_cast<long long>(tokens) * hidden;
+    a.count = count - head;
+    a.head = head;
+    a.elems_per_load = elems;
     a.blocks = p.blocks;
     a.xcd_chunk = p.xcd_chunk;
     int prev = -1;
@@ -533,8 +542,7 @@ int arrms_reduce(arrms_handle_t h, const void* const* partials, int world, int t
         h->last_hip_error = static_cast<int>(hipErrorInvalidDevice);
         return ARRMS_ERR_HIP;
     }
-    const hipError_t e = p.variant == ARRMS_VARIANT_REDUCE ? arrms::launch_reduce(a, p.vec_per_thread, p.grid, p.block, stream)
-                                                           : arrms::launch_reduce_scalar(a, p.grid, p.block, stream);
+    const hipError_t e = arrms::launch_reduce(a, p.vec_per_thread, p.grid, p.block, stream);
     if (prev >= 0 && prev != h->device) (void)hipSetDevice(prev);
     if (e != hipSuccess) {
         h->last_hip_error = static_cast<int>(e);

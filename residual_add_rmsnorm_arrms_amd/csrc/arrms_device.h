@@ -50,6 +50,43 @@ __device__ __forceinline__ void st4_stream(void* base, size_t i, u32x4 v) {
     __builtin_nontemporal_store(v, static_cast<u32x4*>(base) + i);
 }
 
+// ------------------------------------------------- groups of E BF16 elements
+// The unit one load moves: E consecutive BF16 elements (E = 1, 2, 4 or 8: a 2-,
+// 4-, 8- or 16-byte load), with access to element k (k = 0 lowest) and packing of
+// E binary32 values rounded to BF16.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int E> struct Group;
+template <> struct Group<1> {
+    typedef uint16_t T;
+    static __device__ __forceinline__ float get(T g, int) { return lo_f32(g); }
+};
+template <> struct Group<2> {
+    typedef uint32_t T;
+    static __device__ __forceinline__ float get(T g, int k) { return k ? hi_f32(g) : lo_f32(g); }
+};
+template <> struct Group<4> {
+    typedef u32x2 T;
+    static __device__ __forceinline__ float get(T g, int k) { return (k & 1) ? hi_f32(g[k >> 1]) : lo_f32(g[k >> 1]); }
+};
+template <> struct Group<8> {
+    typedef u32x4 T;
+    static __device__ __forceinline__ float get(T g, int k) { return (k & 1) ? hi_f32(g[k >> 1]) : lo_f32(g[k >> 1]); }
+};
+
+template <int E>
+__device__ __forceinline__ typename Group<E>::T pack(const float (&v)[E]) {
+    if constexpr (E == 1) {
+        return cvt1(v[0]);
+    } else if constexpr (E == 2) {
+        return cvt2(v[0], v[1]);
+    } else if constexpr (E == 4) {
+        return u32x2{cvt2(v[0], v[1]), cvt2(v[2], v[3])};
+    } else {
+        return u32x4{cvt2(v[0], v[1]), cvt2(v[2], v[3]), cvt2(v[4], v[5]), cvt2(v[6], v[7])};
+    }
+}
+
 // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on XCD
 // b % 8).  With xcd_chunk = K > 0 the launched grid is a multiple of 8K and
 // the i-th workgroup an XCD receives takes logical block (8 * (i / K) + x) * K

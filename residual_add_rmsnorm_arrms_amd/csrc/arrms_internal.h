@@ -40,8 +40,9 @@ struct Args {
     int chunk_vec;          // split-H: vectors per chunk
     int blocks;             // logical workgroups (the launched grid may add XCD padding)
     int xcd_chunk;          // K > 0: runs of K consecutive blocks per XCD (grid a multiple of 8K)
-    int elems_per_load;     // scalar: BF16 elements per load (1, 2 or 4)
-    long long count;        // rank sum only: elements (tokens * hidden)
+    int elems_per_load;     // scalar: BF16 elements per load (1, 2 or 4); rank sum: 1, 2, 4 or 8
+    int head;               // rank sum only: elements before the aligned start of x.p[] / reduced
+    long long count;        // rank sum only: elements from the aligned start (tokens * hidden - head)
 };
 
 // ------------------------------------------------- per-kernel argument blocks
@@ -118,8 +119,9 @@ struct ScalarArgs {
     uint32_t shape;
 };
 
-// Rank sum alone (256 lanes per workgroup).  grid: launched workgroups (the
-// element-wise kernel's grid stride).
+// Rank sum alone (256 lanes per workgroup).  x and reduced point at the first
+// aligned element; `head` elements before it and the count % E after the last
+// whole group are done element-wise by the last workgroup.
 template <int WA>
 struct ReduceArgs {
     Ptrs<WA> x;
@@ -128,7 +130,7 @@ struct ReduceArgs {
     int blocks;
     int xcd_chunk;
     int world;
-    int grid;
+    int head;
 };
 
 // The first WA partial pointers of a call (the rest of Ptrs<16> stays null).
@@ -151,11 +153,34 @@ hipError_t launch_row(const Args& a, int vec_per_thread, int grid, int block, hi
 // Split-H launches two kernels on `s`: the partial pass, then the norm pass.
 hipError_t launch_splith(const Args& a, int vec_per_thread, int grid, int block, hipStream_t s);
 hipError_t launch_scalar(const Args& a, int grid, int block, hipStream_t s);
-// Rank sum only (reduced = BF16 sum of the partials), flat over a.count elements.
-// reduce_kernel instances: 16-byte vectors per lane per partial of 1, 2 or 4
-// for W <= 8, only 1 for the 16-wide rank arrays of larger W (register budget).
+// Rank sum only (reduced = BF16 sum of the partials), flat over a.head + a.count
+// elements, with loads of a.elems_per_load elements.  16-byte loads (8 elements)
+// take 1, 2 or 4 vectors per lane per partial for W <= 8, only 1 for the 16-wide
+// rank arrays of larger W (register budget); narrower loads take 16 bytes per lane.
 hipError_t launch_reduce(const Args& a, int vec_per_thread, int grid, int block, hipStream_t s);
-hipError_t launch_reduce_scalar(const Args& a, int grid, int block, hipStream_t s);
+
+// Load width of the rank sum, flat over memory: the widest E in {8, 4, 2, 1}, at
+// most max_elems, such that every pointer (the W partials and the output) has the
+// same offset modulo 2E bytes, and the number of elements before the first
+// 2E-aligned one (at most `count`).  Pointers are 2-byte aligned, so E = 1 always
+// qualifies.
+inline void reduce_alignment(const void* const* partials, int world, const void* reduced, long long count,
+                             int max_elems, int* elems, int* head) {
+    const uintptr_t p0 = reinterpret_cast<uintptr_t>(reduced);
+    int e = max_elems >= 8 ? 8 : (max_elems >= 4 ? 4 : (max_elems >= 2 ? 2 : 1));
+    for (; e > 1; e /= 2) {
+        const uintptr_t m = static_cast<uintptr_t>(2 * e - 1);
+        bool same = true;
+        for (int r = 0; r < world; ++r)
+            if (((reinterpret_cast<uintptr_t>(partials[r]) ^ p0) & m) != 0) same = false;
+        if (same) break;
+    }
+    const uintptr_t m = static_cast<uintptr_t>(2 * e - 1);
+    long long h = static_cast<long long>(((2 * e - (p0 & m)) & m) / 2);
+    if (h > count) h = count;
+    *elems = e;
+    *head = static_cast<int>(h);
+}
 
 // Does a planned call's split-H workspace, tokens x chunks_per_row doubles, fit
 // a workspace of `capacity` doubles?  Plans of the other variants use none.

@@ -220,35 +220,6 @@ __global__ void __launch_bounds__(1024) splith_norm_kernel(const SplitNormArgs a
 // push a row that fits one span into a second.
 constexpr int kScalarSpan = 8;
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// Storage of E consecutive BF16 elements, and access to element k of it.
-template <int E> struct Group;
-template <> struct Group<1> {
-    typedef uint16_t T;
-    static __device__ __forceinline__ float get(T g, int) { return lo_f32(g); }
-};
-template <> struct Group<2> {
-    typedef uint32_t T;
-    static __device__ __forceinline__ float get(T g, int k) { return k ? hi_f32(g) : lo_f32(g); }
-};
-template <> struct Group<4> {
-    typedef u32x2 T;
-    static __device__ __forceinline__ float get(T g, int k) { return (k & 1) ? hi_f32(g[k >> 1]) : lo_f32(g[k >> 1]); }
-};
-
-// E binary32 values rounded to BF16 and packed as one group (element 0 lowest).
-template <int E>
-__device__ __forceinline__ typename Group<E>::T pack(const float (&v)[E]) {
-    if constexpr (E == 1) {
-        return cvt1(v[0]);
-    } else if constexpr (E == 2) {
-        return cvt2(v[0], v[1]);
-    } else {
-        return u32x2{cvt2(v[0], v[1]), cvt2(v[2], v[3])};
-    }
-}
-
 // Largest workgroup of a scalar kernel: the generic-W instances keep up to 16 ranks'
 // loads in registers and get the larger register budget of 512-lane workgroups.  The
 // host planner uses the same limits.

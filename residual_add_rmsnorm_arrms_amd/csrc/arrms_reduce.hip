@@ -13,39 +13,72 @@ namespace {
 
 using namespace dev;
 
-// Workgroup size of both rank-sum kernels (the host plans 256 lanes).
+// Workgroup size of the rank-sum kernel (the host plans 256 lanes).
 constexpr int kReduceLanes = 256;
 
 // ------------------------------------------------------------ rank sum only
 // The contract's first line on its own (the page's collective stage, locally):
-// reduced = BF16(sum of the W partials), flat over a.count = T*H elements.
-// Each lane sums VPT 16-byte vectors (at stride 256) of every partial;
-// the last count % 8 elements go element-wise in the last block.
-template <int W, int kReduceVpt>
+// reduced = BF16(sum of the W partials), flat over the T*H elements, so only the
+// pointers' alignment decides the load width.  The host picks the widest width E
+// (8, 4, 2 or 1 elements: 16-, 8-, 4- or 2-byte loads) at which every pointer has
+// the same offset, and passes the pointers advanced to their first E-aligned
+// element.  Each lane sums L groups of E elements (at stride 256) of every
+// partial, all loads issued first; the last workgroup adds the `head` elements
+// before the aligned start and the count % E after the last whole group, element
+// by element.
+template <int W, int L, int E>
 __global__ void __launch_bounds__(kReduceLanes) reduce_kernel(const ReduceArgs<(W > 0 ? W : kMaxWorld)> a) {
+    typedef typename Group<E>::T G;
     constexpr int WA = W > 0 ? W : kMaxWorld;
     const int world = W > 0 ? W : a.world;
     const int block = logical_block(a.xcd_chunk, a.blocks);
     if (block < 0) return;
-    const size_t nvec = static_cast<size_t>(a.count) / 8;
-    const size_t first = static_cast<size_t>(block) * kReduceLanes * kReduceVpt + threadIdx.x;
-    bool ok[kReduceVpt];
-    u32x4 xv[kReduceVpt][WA];
+    const size_t ng = static_cast<size_t>(a.count) / E;
+    const size_t first = static_cast<size_t>(block) * kReduceLanes * L + threadIdx.x;
+    bool ok[L];
+    G xv[L][WA];
+    if (ng > 0) {  // (a call of fewer elements than one group has only its head and tail)
 #pragma unroll
-    for (int k = 0; k < kReduceVpt; ++k) {
-        const size_t v = first + static_cast<size_t>(k) * kReduceLanes;
-        ok[k] = v < nvec;
-        if (ok[k]) {
+        for (int k = 0; k < L; ++k) {
+            const size_t g = first + static_cast<size_t>(k) * kReduceLanes;
+            ok[k] = g < ng;
+            if constexpr (E < 8 && W > 0) {
+                // Narrow loads: from a clamped index where the group lies past the end (its
+                // value is never used), so no branch separates the loads and all of them
+                // issue before the first wait.
+                const size_t gc = g < ng ? g : ng - 1;
 #pragma unroll
-            for (int r = 0; r < WA; ++r)
-                if (W > 0 || r < world) xv[k][r] = ld4_stream(a.x.p[r], v);
+                for (int r = 0; r < WA; ++r)
+                    xv[k][r] = __builtin_nontemporal_load(static_cast<const G*>(a.x.p[r]) + gc);
+            } else if (ok[k]) {
+#pragma unroll
+                for (int r = 0; r < WA; ++r)
+                    if (W > 0 || r < world)
+                        xv[k][r] = __builtin_nontemporal_load(static_cast<const G*>(a.x.p[r]) + g);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < L; ++k) {
+            if (ok[k]) {
+                float sum[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    float acc = Group<E>::get(xv[k][0], e);
+#pragma unroll
+                    for (int r = 1; r < WA; ++r)
+                        if (W > 0 || r < world) acc = acc + Group<E>::get(xv[k][r], e);
+                    sum[e] = acc;
+                }
+                __builtin_nontemporal_store(pack<E>(sum),
+                                            static_cast<G*>(a.reduced) + first + static_cast<size_t>(k) * kReduceLanes);
+            }
         }
     }
-#pragma unroll
-    for (int k = 0; k < kReduceVpt; ++k)
-        if (ok[k]) st4_stream(a.reduced, first + static_cast<size_t>(k) * kReduceLanes, reduced_vec<W>(xv[k], world));
-    if (block == a.blocks - 1) {  // the count % 8 elements past the last whole vector
-        for (size_t e = nvec * 8 + threadIdx.x; e < static_cast<size_t>(a.count); e += kReduceLanes) {
+    if (block == a.blocks - 1) {  // the head and the tail, element-wise
+        const long long tail0 = static_cast<long long>(ng) * E;
+        const int extra = a.head + static_cast<int>(a.count - tail0);
+        for (int j = threadIdx.x; j < extra; j += kReduceLanes) {
+            const long long e = j < a.head ? static_cast<long long>(j - a.head) : tail0 + (j - a.head);
             float acc = lo_f32(static_cast<const uint16_t*>(a.x.p[0])[e]);
             for (int r = 1; r < world; ++r) acc = acc + lo_f32(static_cast<const uint16_t*>(a.x.p[r])[e]);
             static_cast<uint16_t*>(a.reduced)[e] = cvt1(acc);
@@ -53,31 +86,21 @@ __global__ void __launch_bounds__(kReduceLanes) reduce_kernel(const ReduceArgs<(
     }
 }
 
-// Rank sum only, element-wise, for pointers that are not 16-byte aligned.
-__global__ void __launch_bounds__(kReduceLanes) reduce_scalar_kernel(const ReduceArgs<kMaxWorld> a) {
-    const size_t stride = static_cast<size_t>(a.grid) * kReduceLanes;
-    for (size_t e = static_cast<size_t>(blockIdx.x) * kReduceLanes + threadIdx.x; e < static_cast<size_t>(a.count);
-         e += stride) {
-        float acc = lo_f32(static_cast<const uint16_t*>(a.x.p[0])[e]);
-        for (int r = 1; r < a.world; ++r) acc = acc + lo_f32(static_cast<const uint16_t*>(a.x.p[r])[e]);
-        static_cast<uint16_t*>(a.reduced)[e] = cvt1(acc);
-    }
-}
-
-template <int VPT>
+template <int L, int E>
 const void* reduce_fn(int world) {
     switch (world) {
-        case 1: return reinterpret_cast<const void*>(&reduce_kernel<1, VPT>);
-        case 2: return reinterpret_cast<const void*>(&reduce_kernel<2, VPT>);
-        case 3: return reinterpret_cast<const void*>(&reduce_kernel<3, VPT>);
-        case 4: return reinterpret_cast<const void*>(&reduce_kernel<4, VPT>);
-        case 5: return reinterpret_cast<const void*>(&reduce_kernel<5, VPT>);
-        case 6: return reinterpret_cast<const void*>(&reduce_kernel<6, VPT>);
-        case 7: return reinterpret_cast<const void*>(&reduce_kernel<7, VPT>);
-        case 8: return reinterpret_cast<const void*>(&reduce_kernel<8, VPT>);
+        case 1: return reinterpret_cast<const void*>(&reduce_kernel<1, L, E>);
+        case 2: return reinterpret_cast<const void*>(&reduce_kernel<2, L, E>);
+        case 3: return reinterpret_cast<const void*>(&reduce_kernel<3, L, E>);
+        case 4: return reinterpret_cast<const void*>(&reduce_kernel<4, L, E>);
+        case 5: return reinterpret_cast<const void*>(&reduce_kernel<5, L, E>);
+        case 6: return reinterpret_cast<const void*>(&reduce_kernel<6, L, E>);
+        case 7: return reinterpret_cast<const void*>(&reduce_kernel<7, L, E>);
+        case 8: return reinterpret_cast<const void*>(&reduce_kernel<8, L, E>);
         default: break;
     }
-    if constexpr (VPT == 1) return reinterpret_cast<const void*>(&reduce_kernel<0, 1>);
+    // more than 8 ranks: one 16 bytes' worth of groups per lane (register budget)
+    if constexpr (L * E == 8) return reinterpret_cast<const void*>(&reduce_kernel<0, L, E>);
     return nullptr;
 }
 
@@ -90,7 +113,7 @@ hipError_t launch_reduce_with(const void* fn, const Args& a, int grid, hipStream
     r.blocks = a.blocks;
     r.xcd_chunk = a.xcd_chunk;
     r.world = a.world;
-    r.grid = grid;
+    r.head = a.head;
     return launch_with(fn, r, grid, kReduceLanes, s);
 }
 
@@ -98,14 +121,22 @@ hipError_t launch_reduce_with(const void* fn, const Args& a, int grid, hipStream
 
 hipError_t launch_reduce(const Args& a, int vpt, int grid, int block, hipStream_t s) {
     const void* fn = nullptr;
-    switch (vpt) {
-        case 1: fn = reduce_fn<1>(a.world); break;
-        case 2: fn = reduce_fn<2>(a.world); break;
-        case 4: fn = reduce_fn<4>(a.world); break;
+    switch (a.elems_per_load) {
+        case 8:
+            switch (vpt) {
+                case 1: fn = reduce_fn<1, 8>(a.world); break;
+                case 2: fn = reduce_fn<2, 8>(a.world); break;
+                case 4: fn = reduce_fn<4, 8>(a.world); break;
+                default: return hipErrorInvalidValue;
+            }
+            break;
+        case 4: fn = reduce_fn<2, 4>(a.world); break;
+        case 2: fn = reduce_fn<4, 2>(a.world); break;
+        case 1: fn = reduce_fn<8, 1>(a.world); break;
         default: return hipErrorInvalidValue;
     }
-    if (!fn || block != kReduceLanes) return hipErrorInvalidValue;
-    // reduce_kernel<W, VPT> takes ReduceArgs<W> for W <= 8 and ReduceArgs<16> otherwise
+    if (!fn || block != kReduceLanes || a.head < 0 || a.head >= a.elems_per_load) return hipErrorInvalidValue;
+    // reduce_kernel<W, L, E> takes ReduceArgs<W> for W <= 8 and ReduceArgs<16> otherwise
     switch (a.world) {
         case 1: return launch_reduce_with<1>(fn, a, grid, s);
         case 2: return launch_reduce_with<2>(fn, a, grid, s);
@@ -117,11 +148,6 @@ hipError_t launch_reduce(const Args& a, int vpt, int grid, int block, hipStream_
         case 8: return launch_reduce_with<8>(fn, a, grid, s);
         default: return launch_reduce_with<kMaxWorld>(fn, a, grid, s);
     }
-}
-
-hipError_t launch_reduce_scalar(const Args& a, int grid, int block, hipStream_t s) {
-    if (block != kReduceLanes) return hipErrorInvalidValue;
-    return launch_reduce_with<kMaxWorld>(reinterpret_cast<const void*>(&reduce_scalar_kernel), a, grid, s);
 }
 
 }  // namespace arrms

@@ -15,7 +15,6 @@ hipError_t launch_row(const Args&, int, int, int, hipStream_t) { return hipError
 hipError_t launch_splith(const Args&, int, int, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_scalar(const Args&, int, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_reduce(const Args&, int, int, int, hipStream_t) { return hipErrorInvalidValue; }
-hipError_t launch_reduce_scalar(const Args&, int, int, hipStream_t) { return hipErrorInvalidValue; }
 }  // namespace arrms
 
 static uint64_t state = 0x243F6A8885A308D3ull;
@@ -108,11 +107,21 @@ int main(int argc, char** argv) {
         if (rc2 == ARRMS_OK && T > 0 && p.grid > 0) {
             const long long count = (long long)T * H;
             if ((long long)p.grid * p.block > 0xffffffffLL) return fail("reduce grid limit", i);
-            if (p.variant == ARRMS_VARIANT_REDUCE) {
-                if ((long long)p.blocks * p.block * p.vec_per_thread < count / 8) return fail("reduce cover", i);
-            } else if (p.variant != ARRMS_VARIANT_REDUCE_SCALAR) {
-                return fail("reduce variant", i);
-            }
+            const int e = p.elems_per_load;
+            if (!(e == 1 || e == 2 || e == 4 || e == 8)) return fail("reduce load width", i);
+            if ((p.variant == ARRMS_VARIANT_REDUCE) != (e == 8)) return fail("reduce variant", i);
+            if (p.variant != ARRMS_VARIANT_REDUCE && p.variant != ARRMS_VARIANT_REDUCE_SCALAR)
+                return fail("reduce variant kind", i);
+            // every pointer has the same offset modulo 2E bytes, and the groups cover the elements
+            int e2 = 0, head = -1;
+            arrms::reduce_alignment(parts, W, no, count, e, &e2, &head);
+            if (e2 != e || head < 0 || head >= e || head > count) return fail("reduce alignment", i);
+            // (a head cut short by a tiny count leaves no groups, so nothing to align)
+            for (int r = 0; r < W && head < count; ++r)
+                if ((((uintptr_t)parts[r] + 2u * head) | ((uintptr_t)no + 2u * head)) & (uintptr_t)(2 * e - 1))
+                    return fail("reduce aligned start", i);
+            const long long per_block = 256LL * (e == 8 ? p.vec_per_thread : 8 / e);
+            if ((long long)p.blocks * per_block < (count - head) / e) return fail("reduce cover", i);
         }
     }
     printf("plan fuzz ok: %d iterations\n", iters);

@@ -307,7 +307,7 @@ def test_measured_automatic_choices(W, T, H, variant, vpt, tpr, k):
 
 def rplan(W, T, H, lim=LIM, **over):
     b = bufs(W, T, H)
-    b.update(over)
+    b.update(over)  # partials / reduced may be given
     return A.arrms_plan_reduce(CU, None, lim["max_world"], lim["max_tokens"], lim["max_hidden"], b["partials"], W, T,
                                H, b.get("reduced", b["residual_out"]))
 
@@ -320,6 +320,28 @@ def test_reduce_plans_cover_every_element(W, T, H):
     per_block = p["block"] * p["vec_per_thread"]
     assert p["blocks"] == max(1, -(-nvec // per_block)) and p["grid"] == grid_of(p)
     assert p["vec_per_thread"] == 1
+
+
+@pytest.mark.parametrize("part_off,out_off,elems", [
+    (0, 0, 8), (2, 2, 8), (14, 14, 8), (8, 8, 8),      # the same offset everywhere: 16-byte loads after a head
+    (0, 8, 4), (8, 0, 4), (0, 4, 2), (4, 12, 4), (0, 2, 1), (6, 0, 1), (2, 10, 4),
+])
+def test_reduce_load_width(part_off, out_off, elems):
+    """The rank sum is flat: the widest load at which every pointer has the same offset."""
+    b = bufs(4, 16, 2048)
+    parts = [p + part_off for p in b["partials"]]
+    rc, p = rplan(4, 16, 2048, partials=parts, reduced=b["residual_out"] + out_off)
+    assert rc == A.ARRMS_OK and p["elems_per_load"] == elems
+    assert p["variant"] == (A.ARRMS_VARIANT_REDUCE if elems == 8 else A.ARRMS_VARIANT_REDUCE_SCALAR)
+    assert p["vec_per_thread"] == (1 if elems == 8 else 0)
+
+
+def test_reduce_load_width_tuning():
+    b = bufs(4, 16, 2048)
+    for cap in (1, 2, 4):
+        rc, p = A.arrms_plan_reduce(CU, A.arrms_tuning_t.make(scalar_elems=cap), 16, 20000, 65536, b["partials"], 4,
+                                    16, 2048, b["residual_out"])
+        assert rc == A.ARRMS_OK and p["elems_per_load"] == cap and p["variant"] == A.ARRMS_VARIANT_REDUCE_SCALAR
 
 
 def test_reduce_plan_validation():

@@ -50,23 +50,64 @@ def test_reduce_in_place_into_a_partial():
     assert np.array_equal(synth.bits(out.cpu()), reference(x, res, w, 1e-6)["reduced"])
 
 
-def test_reduce_misaligned_uses_element_path():
-    say("case reduce misaligned")
-    W, T, H = 3, 11, 2048
-    x, res, w = inputs(W, T, H, seed=302)
-    n = T * H
-    parts = []
-    for r in range(W):
-        buf = torch.zeros(n + 8, dtype=torch.bfloat16, device=DEV)
-        v = buf[1:1 + n].view(T, H)
-        v.copy_(x[r].to(DEV))
-        parts.append(v)
-    out = torch.zeros(n + 8, dtype=torch.bfloat16, device=DEV)[1:1 + n].view(T, H)
-    rc, plan = A.arrms_plan_reduce(256, None, 16, 20000, 65536, [p.data_ptr() for p in parts], W, T, H, out.data_ptr())
-    assert rc == A.ARRMS_OK and plan["variant"] == A.ARRMS_VARIANT_REDUCE_SCALAR
+def _placed(t, off_bytes):
+    """A GPU copy of CPU tensor t whose data starts off_bytes after a 256-byte boundary."""
+    n = t.numel()
+    buf = torch.zeros(n + 256, dtype=torch.bfloat16, device=DEV)
+    base = (-buf.data_ptr()) % 256 // 2
+    view = buf[base + off_bytes // 2: base + off_bytes // 2 + n].view(t.shape)
+    view.copy_(t.to(DEV))
+    assert view.data_ptr() % 256 == off_bytes
+    return view
+
+
+# The rank sum is flat over T*H elements: with every tensor at the same offset it
+# loads 16 bytes at a time after a head of up to 7 elements; where the offsets differ
+# it takes the widest load at which they agree (8, 4 or 2 bytes).
+@pytest.mark.parametrize("W,T,H,part_off,out_off,elems", [
+    (3, 11, 2048, 2, 2, 8), (3, 11, 2048, 14, 14, 8), (4, 64, 1000, 8, 8, 8), (2, 4096, 2048, 6, 6, 8),
+    (4, 33, 2048, 0, 8, 4), (4, 33, 2048, 0, 4, 2), (4, 33, 2048, 0, 2, 1), (4, 33, 2047, 8, 0, 4),
+    (1, 1, 3, 2, 2, 8), (1, 1, 5, 0, 4, 2), (2, 3, 5, 0, 6, 1), (16, 7, 999, 6, 6, 8), (9, 5, 2049, 0, 12, 2), (12, 300, 1000, 4, 0, 2),
+    (8, 513, 5120, 2, 0, 1),
+])
+def test_reduce_at_offsets(W, T, H, part_off, out_off, elems):
+    say("case reduce offsets W=%d T=%d H=%d partials +%d out +%d" % (W, T, H, part_off, out_off))
+    x, res, w = inputs(W, T, H, seed=302 + W + T + part_off + out_off, outlier_p=0.01)
+    parts = [_placed(x[r], part_off) for r in range(W)]
+    out = _placed(torch.zeros(T, H, dtype=torch.bfloat16), out_off)
+    rc, plan = A.arrms_plan_reduce(256, None, 16, 20000, 65536, [p.data_ptr() for p in parts], W, T, H,
+                                   out.data_ptr())
+    assert rc == A.ARRMS_OK and plan["elems_per_load"] == elems
+    assert plan["variant"] == (A.ARRMS_VARIANT_REDUCE if elems == 8 else A.ARRMS_VARIANT_REDUCE_SCALAR)
     op().reduce(parts, out)
     torch.cuda.synchronize()
     assert np.array_equal(synth.bits(out.cpu()), reference(x, res, w, 1e-6)["reduced"])
+
+
+@pytest.mark.parametrize("off", [0, 6])
+def test_reduce_in_place_at_an_offset(off):
+    say("case reduce in place at +%d" % off)
+    W, T, H = 4, 17, 1003
+    x, res, w = inputs(W, T, H, seed=305 + off)
+    parts = [_placed(x[r], off) for r in range(W)]
+    out = op().reduce(parts, reduced=parts[1])
+    torch.cuda.synchronize()
+    assert np.array_equal(synth.bits(out.cpu()), reference(x, res, w, 1e-6)["reduced"])
+
+
+@pytest.mark.parametrize("elems", [1, 2, 4])
+@pytest.mark.parametrize("W", [3, 8, 11])
+def test_reduce_tuned_load_widths(elems, W):
+    """Tuning caps the load width: the same aligned tensors through 2-, 4- and 8-byte loads."""
+    say("case reduce width %d W=%d" % (elems, W))
+    x, res, w = inputs(W, 129, 1000, seed=320 + W + elems)
+    o = op()
+    o.set_tuning(scalar_elems=elems)
+    try:
+        got = reduce_gpu(x)
+    finally:
+        o.set_tuning()
+    assert np.array_equal(got, reference(x, res, w, 1e-6)["reduced"])
 
 
 @pytest.mark.parametrize("W,T,H", [(4, 4096, 2048), (8, 129, 5120), (2, 4, 128)])
