@@ -375,14 +375,14 @@ int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
     int split_max = (tuning && tuning->splith_max_tokens >= 0) ? tuning->splith_max_tokens
                                                               : auto_splith_max_tokens(cu_count, world, hidden);
     // The automatic choice always finds a plan: tuning overrides that no vector
-    // kernel can honour end in the element-wise kernel (same results).
+    // kernel can honour end in the scalar kernel (same results).
     if (hidden > ARRMS_ROW_MAX_HIDDEN || tokens <= split_max) {
         if (plan_splith(cu_count, max_hidden, world, tokens, hidden, tuning, plan) == ARRMS_OK) return ARRMS_OK;
         memset(plan, 0, sizeof *plan);
     }
     if (hidden <= ARRMS_ROW_MAX_HIDDEN && plan_row(cu_count, world, tokens, hidden, tuning, plan) == ARRMS_OK)
         return ARRMS_OK;
-    // A row the row kernels cannot hold in registers: split it, else go element-wise.
+    // A row the row kernels cannot hold in registers: split it, else take the scalar kernel.
     memset(plan, 0, sizeof *plan);
     if (plan_splith(cu_count, max_hidden, world, tokens, hidden, tuning, plan) == ARRMS_OK) return ARRMS_OK;
     memset(plan, 0, sizeof *plan);

@@ -407,7 +407,7 @@ def test_tuned_rows_per_block_keeps_one_vector_layout():
 @pytest.mark.parametrize("tuning", [dict(vec_per_thread=4), dict(vec_per_thread=8), dict(splith_block=64)])
 def test_automatic_choice_never_fails_under_tuning(tuning):
     """Tuning changes speed only: where no vector kernel can honour it, the automatic
-    choice ends in the element-wise kernel instead of refusing the call."""
+    choice ends in the scalar kernel instead of refusing the call."""
     for W, T, H in ((4, 3, 32768), (4, 5000, 65536), (8, 2, 8192), (4, 4096, 2048)):
         rc, p = plan(W, T, H, tuning=A.arrms_tuning_t.make(**tuning))
         assert rc == A.ARRMS_OK, (W, T, H, tuning)

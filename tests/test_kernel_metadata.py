@@ -49,6 +49,6 @@ def test_kernel_code_objects(src, tmp_path):
         hidden = [a[".value_kind"] for a in k.get(".args", []) if a[".value_kind"].startswith("hidden")]
         assert not hidden, (name, hidden)
         w = _world(name)
-        generic = w in (0, 16) or "reduce_scalar_kernel" in name
+        generic = w in (0, 16)
         if not generic:
             assert k[".kernarg_segment_size"] <= MAX_FAST_ARGS, (name, k[".kernarg_segment_size"])
