@@ -210,43 +210,18 @@ class BoundCall:
 
 
 
-class FusedReduceResidualRMSNorm:
-    """Reusable operator over one handle.  Tensors: BF16, on the handle's GPU.
+class _TensorArgs:
+    """Checks of the torch tensors of a call (BF16, contiguous, on `device`, shapes) and
+    their device pointers; shared by the operator and fused_noalloc."""
 
-    ``op(partials, residual, weight, eps, residual_out=None, norm_out=None)`` enqueues
-    the fused call on torch's current stream and returns (residual_out, norm_out).
-    ``partials`` is a [W, T, H] tensor or a sequence of W [T, H] tensors.
-
-    One handle serves one call at a time (the split-H variant uses the handle's
-    workspace): calls on the same stream are ordered by it, but calls on different
-    streams must not overlap.  Use one operator per stream for concurrent streams.
-    """
-
-    def __init__(self, max_world: int, max_tokens: int, max_hidden: int, device: Optional[int] = None):
-        import torch
-        self.device = torch.cuda.current_device() if device is None else int(device)
-        rc, h = arrms_create(self.device, max_world, max_tokens, max_hidden)
-        if rc != ARRMS_OK:
-            raise ArrmsError(rc, "arrms_create")
-        self.handle = h
-
-    def set_variant(self, variant: int) -> None:
-        rc = arrms_set_variant(self.handle, variant)
-        if rc != ARRMS_OK:
-            raise ArrmsError(rc, "arrms_set_variant")
-
-    def set_tuning(self, **kw) -> None:
-        t = arrms_tuning_t.make(**kw) if kw else None
-        rc = arrms_set_tuning(self.handle, t)
-        if rc != ARRMS_OK:
-            raise ArrmsError(rc, "arrms_set_tuning")
+    device: int
 
     def _check(self, t, name, shape=None):
         import torch
         if t.dtype != torch.bfloat16 or not t.is_cuda:
             raise TypeError("%s must be a bfloat16 GPU tensor" % name)
         if t.device.index != self.device:
-            raise ValueError("%s is on cuda:%s, the handle on cuda:%d" % (name, t.device.index, self.device))
+            raise ValueError("%s is on cuda:%s, the call runs on cuda:%d" % (name, t.device.index, self.device))
         if not t.is_contiguous():
             raise ValueError("%s must be contiguous" % name)
         if shape is not None and tuple(t.shape) != tuple(shape):
@@ -282,6 +257,38 @@ class FusedReduceResidualRMSNorm:
         self._check(residual_out, "residual_out", (T, H))
         self._check(norm_out, "norm_out", (T, H))
         return parts, T, H, residual_out, norm_out
+
+
+class FusedReduceResidualRMSNorm(_TensorArgs):
+    """Reusable operator over one handle.  Tensors: BF16, on the handle's GPU.
+
+    ``op(partials, residual, weight, eps, residual_out=None, norm_out=None)`` enqueues
+    the fused call on torch's current stream and returns (residual_out, norm_out).
+    ``partials`` is a [W, T, H] tensor or a sequence of W [T, H] tensors.
+
+    One handle serves one call at a time (the split-H variant uses the handle's
+    workspace): calls on the same stream are ordered by it, but calls on different
+    streams must not overlap.  Use one operator per stream for concurrent streams.
+    """
+
+    def __init__(self, max_world: int, max_tokens: int, max_hidden: int, device: Optional[int] = None):
+        import torch
+        self.device = torch.cuda.current_device() if device is None else int(device)
+        rc, h = arrms_create(self.device, max_world, max_tokens, max_hidden)
+        if rc != ARRMS_OK:
+            raise ArrmsError(rc, "arrms_create")
+        self.handle = h
+
+    def set_variant(self, variant: int) -> None:
+        rc = arrms_set_variant(self.handle, variant)
+        if rc != ARRMS_OK:
+            raise ArrmsError(rc, "arrms_set_variant")
+
+    def set_tuning(self, **kw) -> None:
+        t = arrms_tuning_t.make(**kw) if kw else None
+        rc = arrms_set_tuning(self.handle, t)
+        if rc != ARRMS_OK:
+            raise ArrmsError(rc, "arrms_set_tuning")
 
     def plan(self, partials, residual, weight, eps, residual_out=None, norm_out=None) -> dict:
         parts, T, H, residual_out, norm_out = self._args(partials, residual, weight, residual_out, norm_out)
@@ -346,3 +353,23 @@ class FusedReduceResidualRMSNorm:
 
     def __exit__(self, *exc):
         self.close()
+
+
+def fused_noalloc(partials, residual, weight, eps: float, residual_out, norm_out, stream=None):
+    """arrms_fused_noalloc on torch tensors: the fused call on the current device with no
+    handle and no allocation of any kind (for code under graph capture or in serving
+    loops).  Both outputs must be given; tensors as for FusedReduceResidualRMSNorm.
+    The first call on a device looks up its static scratch and should be made outside
+    graph capture.  Returns (residual_out, norm_out)."""
+    import torch
+    if residual_out is None or norm_out is None:
+        raise ValueError("fused_noalloc allocates nothing: pass residual_out and norm_out")
+    args = _TensorArgs()
+    args.device = torch.cuda.current_device()
+    parts, T, H, residual_out, norm_out = args._args(partials, residual, weight, residual_out, norm_out)
+    s = (stream if stream is not None else torch.cuda.current_stream(args.device)).cuda_stream
+    rc = arrms_fused_noalloc(parts, len(parts), T, H, residual.data_ptr(), weight.data_ptr(), eps,
+                             residual_out.data_ptr(), norm_out.data_ptr(), s)
+    if rc != ARRMS_OK:
+        raise ArrmsError(rc, "arrms_fused_noalloc")
+    return residual_out, norm_out

@@ -453,3 +453,16 @@ def test_operator_checks_tensor_arguments():
     x = torch.zeros((2, 4, 16), dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         op._args(x, torch.zeros((4, 16), dtype=torch.bfloat16), torch.zeros(16, dtype=torch.bfloat16), None, None)
+
+
+def test_fused_noalloc_wrapper_needs_both_outputs():
+    """The torch-level no-allocation call allocates nothing, so it refuses missing outputs
+    before touching any device."""
+    import torch
+    x = torch.zeros((2, 4, 16), dtype=torch.bfloat16)
+    r = torch.zeros((4, 16), dtype=torch.bfloat16)
+    w = torch.zeros(16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="allocates nothing"):
+        A.fused_noalloc(x, r, w, 1e-6, None, torch.zeros_like(r))
+    with pytest.raises(ValueError, match="allocates nothing"):
+        A.fused_noalloc(x, r, w, 1e-6, torch.zeros_like(r), None)

@@ -127,3 +127,13 @@ def test_errors_match_arrms_fused():
     assert f(parts, 2, 4, 128, res, w, 1e-6, parts[1], no, s) == A.ARRMS_ERR_INVALID_ARG
     assert f(None, 2, 4, 128, res, w, 1e-6, ro, no, s) == A.ARRMS_ERR_INVALID_ARG
     torch.cuda.synchronize(DEV)
+
+
+def test_torch_level_wrapper_matches_arrms_fused():
+    """fused_noalloc (torch tensors, the current device) gives arrms_fused's bits."""
+    c = Case(4, 77, 2048, seed=21)
+    say("fused_noalloc (torch level) W=4 T=77 H=2048")
+    ro, no = A.fused_noalloc(c.xd, c.rd, c.wd, c.eps, c.ro["static"], c.no["static"])
+    assert ro.data_ptr() == c.ro["static"].data_ptr() and no.data_ptr() == c.no["static"].data_ptr()
+    assert c.call_handle() == A.ARRMS_OK
+    c.check()
