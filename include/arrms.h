@@ -82,6 +82,8 @@ typedef struct {
     int xcd_chunk;       /* K > 0: runs of K consecutive workgroups (rows) kept on one XCD; 0: hardware order */
     int elems_per_load;  /* scalar: BF16 elements per load (4, 2 or 1: 8-, 4- or 2-byte loads); rank sum: 8, 4,
                             2 or 1; else 0 */
+    int residual_out_cached; /* 1: residual_out written with write-back stores, 0: with streaming (non-temporal)
+                                stores; split-H always 1 (its second kernel reads residual_out back); rank sum 0 */
 } arrms_plan_t;
 
 /* Optional tuning overrides; 0 (or -1 where stated) keeps the automatic choice.
@@ -94,6 +96,7 @@ typedef struct {
     int xcd_chunk;         /* -1 automatic; 0 hardware round-robin; K > 0 runs of K blocks per XCD */
     int rows_per_block;    /* row: token rows per workgroup (power of two); 0 automatic */
     int scalar_elems;      /* scalar and rank sum: at most this many BF16 elements per load (1, 2 or 4); 0 automatic */
+    int residual_out_store; /* row and scalar: 0 automatic, 1 streaming stores, 2 write-back stores */
 } arrms_tuning_t;
 
 /*

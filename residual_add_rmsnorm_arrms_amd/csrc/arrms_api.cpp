@@ -46,6 +46,16 @@ constexpr long kXcdRunBytes = 3L << 20;
 constexpr int kReduceAutoVpt = 1;
 // Rows with less traffic than this never use split-H automatically.
 constexpr long kSplitMinRowBytes = 144L << 10;
+// Store policy of residual_out in the row and scalar kernels (measured on MI355X
+// with the row kernel over 87 shapes, W = 1..16, H = 1024..16384, T = 2048..16384,
+// back-to-back calls on buffers beyond the Infinity Cache): write-back stores beat
+// streaming ones by 2-9 % while a call writes at most 128 MiB of residual_out, half
+// the 256 MB Infinity Cache, and lose up to 11 % above it; with one or two ranks
+// they also lose, up to 12 %, below 24 MiB (those calls run four rows per
+// workgroup).  The rule below is never more than 2.3 % slower than streaming stores
+// on any measured shape (W = 8 and 16 at 16-32 MiB lose 1-2.3 %).
+constexpr long long kRoCachedMaxBytes = 128LL << 20;
+constexpr long long kRoCachedFewRanksMinBytes = 24LL << 20;
 
 int chunks_capacity(int max_hidden) {
     const int nvec = (max_hidden + 7) / 8;
@@ -88,7 +98,17 @@ bool valid_tuning(const arrms_tuning_t* t) {
     if (rp < 0 || rp > 64 || (rp & (rp - 1))) return false;
     const int se = t->scalar_elems;
     if (!(se == 0 || se == 1 || se == 2 || se == 4)) return false;
+    if (t->residual_out_store < 0 || t->residual_out_store > 2) return false;
     return true;
+}
+
+// Write-back (1) or streaming (0) stores for residual_out in the row and scalar kernels.
+int residual_out_cached(int world, int tokens, int hidden, const arrms_tuning_t* t) {
+    if (t && t->residual_out_store) return t->residual_out_store == 2;
+    const long long bytes = 2LL * tokens * hidden;
+    if (bytes > kRoCachedMaxBytes) return 0;
+    if (world <= 2 && bytes < kRoCachedFewRanksMinBytes) return 0;
+    return 1;
 }
 
 // Launch shape of a vector-variant plan whose logical workgroup count is
@@ -168,6 +188,7 @@ int plan_row(int cu_count, int world, int tokens, int hidden, const arrms_tuning
     p->block = best_tpr * rpb;
     p->blocks = static_cast<int>((static_cast<long>(tokens) + rpb - 1) / rpb);
     p->kernels = 1;
+    p->residual_out_cached = residual_out_cached(world, tokens, hidden, t);
     // Automatic XCD runs: about 3 MiB of traffic per run, a power of two of
     // blocks (measured best: 64 blocks at W=4 H=2048, 16 at W=8 H=5120/8192);
     // small grids keep the hardware order.
@@ -223,6 +244,7 @@ int plan_splith(int cu_count, int max_hidden, int world, int tokens, int hidden,
     p->block = block;
     p->blocks = tokens * chunks;
     p->kernels = 2;
+    p->residual_out_cached = 1;  // the second kernel reads residual_out back
     finish_vector_plan(t, p, 0);
     return ARRMS_OK;
 }
@@ -232,14 +254,11 @@ int plan_splith(int cu_count, int max_hidden, int world, int tokens, int hidden,
 // ranks: the kernels' __launch_bounds__).  Loads are `elems` BF16
 // elements wide (the widest that H and every pointer's alignment allow, at most
 // the tuned width).  XCD runs as in the row variant (about 3 MiB of traffic per run).
-// Unless every row of the first partial starts on a 128-byte line, the kernel
-// shifts its lanes by up to 63 elements to cover whole lines; the span leaves
-// room for that shift.
-void plan_scalar(int world, int tokens, int hidden, int elems, const void* first_partial, const arrms_tuning_t* t,
-                 arrms_plan_t* p) {
+// The kernel aligns its lanes to 128-byte lines by rotating a one-span row, so a
+// row takes no lanes beyond its own length.
+void plan_scalar(int world, int tokens, int hidden, int elems, const arrms_tuning_t* t, arrms_plan_t* p) {
     const int max_block = world > 8 ? 512 : 1024;
-    const bool lines = (reinterpret_cast<uintptr_t>(first_partial) & 127u) == 0 && hidden % 64 == 0;
-    int block = ((hidden + (lines ? 0 : 63) + 7) / 8 + 63) / 64 * 64;
+    int block = ((hidden + 7) / 8 + 63) / 64 * 64;
     if (block > max_block) block = max_block;
     if (t && t->scalar_elems && t->scalar_elems < elems) elems = t->scalar_elems;
     p->variant = ARRMS_VARIANT_SCALAR;
@@ -251,6 +270,7 @@ void plan_scalar(int world, int tokens, int hidden, int elems, const void* first
     p->blocks = tokens;
     p->kernels = 1;
     p->elems_per_load = elems;
+    p->residual_out_cached = residual_out_cached(world, tokens, hidden, t);
     int k = 0;
     if (p->blocks >= 64) {
         const long row_bytes = 2L * (world + 3) * hidden;
@@ -357,7 +377,7 @@ int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
     const int elems = scalar_elems(hidden, any);
     switch (variant) {
         case ARRMS_VARIANT_SCALAR:
-            plan_scalar(world, tokens, hidden, elems, partials[0], tuning, plan);
+            plan_scalar(world, tokens, hidden, elems, tuning, plan);
             return ARRMS_OK;
         case ARRMS_VARIANT_ROW:
             if (!vector_ok || hidden > ARRMS_ROW_MAX_HIDDEN) return ARRMS_ERR_UNSUPPORTED;
@@ -369,7 +389,7 @@ int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
             break;
     }
     if (!vector_ok) {
-        plan_scalar(world, tokens, hidden, elems, partials[0], tuning, plan);
+        plan_scalar(world, tokens, hidden, elems, tuning, plan);
         return ARRMS_OK;
     }
     int split_max = (tuning && tuning->splith_max_tokens >= 0) ? tuning->splith_max_tokens
@@ -386,7 +406,7 @@ int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
     memset(plan, 0, sizeof *plan);
     if (plan_splith(cu_count, max_hidden, world, tokens, hidden, tuning, plan) == ARRMS_OK) return ARRMS_OK;
     memset(plan, 0, sizeof *plan);
-    plan_scalar(world, tokens, hidden, elems, partials[0], tuning, plan);
+    plan_scalar(world, tokens, hidden, elems, tuning, plan);
     return ARRMS_OK;
 }
 
@@ -484,6 +504,7 @@ hipError_t launch_fused(const arrms_plan_t& p, const void* const* partials, int 
     a.blocks = p.blocks;
     a.xcd_chunk = p.xcd_chunk;
     a.elems_per_load = p.elems_per_load;
+    a.ro_cached = p.residual_out_cached;
     switch (p.variant) {
         case ARRMS_VARIANT_ROW: return launch_row(a, p.vec_per_thread, p.grid, p.block, stream);
         case ARRMS_VARIANT_SPLITH: return launch_splith(a, p.vec_per_thread, p.grid, p.block, stream);

@@ -87,6 +87,49 @@ __device__ __forceinline__ typename Group<E>::T pack(const float (&v)[E]) {
     }
 }
 
+// ----------------------------------------------------- buffer-resource access
+// A buffer resource describes `bytes` bytes from `base`; an access through it at a
+// 32-bit byte offset is checked by the hardware against that range: a load outside
+// it returns zero and a store outside it is dropped (the raw-buffer range check of
+// the GCN/CDNA buffer instructions; the offset is a VGPR, no SGPR offset is used).
+// The fourth descriptor word, 0x00020000, is the 32-bit data format that untyped
+// buffer accesses need on this GPU family.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, 0x00020000);
+}
+
+// Cache-policy operand of the buffer instructions: the non-temporal (streaming) bit.
+constexpr int kBufNT = 2;
+
+// Loads and stores of one E-element group at a byte offset; AUX = kBufNT or 0.
+template <int E> struct Buf;
+template <> struct Buf<1> {
+    template <int AUX> static __device__ __forceinline__ uint16_t ld(Rsrc r, int off) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, AUX);
+    }
+    template <int AUX> static __device__ __forceinline__ void st(uint16_t v, Rsrc r, int off) {
+        __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, AUX);
+    }
+};
+template <> struct Buf<2> {
+    template <int AUX> static __device__ __forceinline__ uint32_t ld(Rsrc r, int off) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
+    }
+    template <int AUX> static __device__ __forceinline__ void st(uint32_t v, Rsrc r, int off) {
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, AUX);
+    }
+};
+template <> struct Buf<4> {
+    typedef decltype(__builtin_amdgcn_raw_buffer_load_b64(Rsrc(), 0, 0, 0)) Raw;
+    template <int AUX> static __device__ __forceinline__ u32x2 ld(Rsrc r, int off) {
+        return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX));
+    }
+    template <int AUX> static __device__ __forceinline__ void st(u32x2 v, Rsrc r, int off) {
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(Raw, v), r, off, 0, AUX);
+    }
+};
+
 // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on XCD
 // b % 8).  With xcd_chunk = K > 0 the launched grid is a multiple of 8K and
 // the i-th workgroup an XCD receives takes logical block (8 * (i / K) + x) * K

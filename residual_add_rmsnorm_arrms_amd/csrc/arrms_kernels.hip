@@ -45,7 +45,7 @@ constexpr int row_max_threads() {
     return (W == 0 || W > 8) ? (VPT == 1 ? 512 : 256) : (VPT == 1 ? 1024 : (VPT <= 4 ? 512 : 256));
 }
 
-template <int W, int VPT>
+template <int W, int VPT, bool RC>
 __global__ void __launch_bounds__((row_max_threads<W, VPT>())) row_kernel(const RowArgs<(W > 0 ? W : kMaxWorld)> a) {
     constexpr int WA = W > 0 ? W : kMaxWorld;
     const int world = W > 0 ? W : static_cast<int>((a.shape >> 26) & 31u);
@@ -85,7 +85,11 @@ __global__ void __launch_bounds__((row_max_threads<W, VPT>())) row_kernel(const 
     for (int k = 0; k < VPT; ++k) {
         if (ok[k]) {
             ro[k] = residual_vec<W>(xv[k], world, rv[k], ss);
-            st4_stream(a.residual_out, base + lane + k * tpr, ro[k]);
+            if constexpr (RC) {
+                st4(a.residual_out, base + lane + k * tpr, ro[k]);
+            } else {
+                st4_stream(a.residual_out, base + lane + k * tpr, ro[k]);
+            }
         }
     }
 
@@ -204,20 +208,32 @@ __global__ void __launch_bounds__(1024) splith_norm_kernel(const SplitNormArgs a
 // the row variant.  The row is walked in spans of kScalarSpan * n elements; in a
 // span lane l owns the E-element groups l, l + n, ..., l + (8 / E - 1) * n, so each
 // load instruction of a wave covers 128 * E contiguous bytes and a lane moves 16
-// bytes per input per span, as in the row variant.  Group indexes past the row are
-// clamped for loads (which then stay inside the row, in one basic block, so the
-// compiler issues the span's loads of every rank together) and masked for stores
-// and for the sum of squares; what a clamped load returns is never used.  When the
-// row fits one span, residual_out stays in registers for the second pass;
-// otherwise the second pass re-reads it (each group is read back by the lane that
-// stored it).
+// bytes per input per span, as in the row variant.
+//
+// Every access goes through a buffer resource spanning one row of its tensor (the
+// weight's whole H elements), so the hardware's range check does the masking: a
+// group index before or past the row loads zeros, which add nothing to the sum of
+// squares, and stores nothing.  No index is clamped, no store is under a branch,
+// and one 32-bit byte offset per group serves every tensor: at 2-byte loads this
+// kernel's time follows its instruction count, and 64-bit per-tensor addresses,
+// clamps and store branches cost it more than the memory traffic.  All loads of a
+// span are issued before its arithmetic.  When the row fits one span,
+// residual_out stays in registers for the second pass; otherwise the second pass
+// re-reads it (each group is read back by the lane that stored it).
+//
 // A row whose start is not on a 128-byte line (odd H, or a pointer offset) would
 // make every wave instruction straddle two lines.  So the lanes' group indexes are
-// shifted back by the row's offset within its line of the first partial: index i
-// takes group i - shift, the wave instructions then cover whole lines of every
-// tensor that is aligned like that partial, and indexes before the row start are
-// clamped and masked like those past its end.  The shift is dropped where it would
-// push a row that fits one span into a second.
+// moved back by the row's offset within its line of the first partial (`shift`
+// groups); the wave instructions then cover whole lines of every tensor aligned
+// like that partial.  A row that fits one span is rotated: index i takes group
+// (i - shift) mod span, a one-to-one map of the span, so the last `shift` groups
+// go to the first lanes and only wave 0's first instruction touches two lines (the
+// row's first and last); the row needs no lanes beyond its own length.  (Extra
+// lanes for the shift cost more than the straddling: 5-wave workgroups on rows of
+// 2048 elements were 18 % slower than 4-wave ones on MI355X.)  A longer row is
+// shifted instead: index i takes group i - shift over ng + shift indexes, and the
+// indexes before the row start fall outside its range.  Since shift < 64 <= n, only
+// a lane's first group of the first span can wrap or fall before the row.
 constexpr int kScalarSpan = 8;
 
 // Largest workgroup of a scalar kernel: the generic-W instances keep up to 16 ranks'
@@ -226,10 +242,12 @@ constexpr int kScalarSpan = 8;
 template <int W>
 constexpr int scalar_max_threads() { return W == 0 ? 512 : 1024; }
 
-template <int W, int E>
+template <int W, int E, bool RC>
 __global__ void __launch_bounds__(scalar_max_threads<W>()) scalar_kernel(const ScalarArgs<(W > 0 ? W : kMaxWorld)> a) {
     typedef typename Group<E>::T G;
+    typedef Buf<E> B;
     constexpr int S = kScalarSpan / E;  // groups per lane per input in a span
+    constexpr int WL = W > 0 ? W : 1;   // ranks whose loads a span keeps in registers
     const int world = W > 0 ? W : static_cast<int>((a.shape >> 22) & 31u);
     const int row = logical_block(a.xcd_chunk, a.tokens);
     if (row < 0) return;  // padding workgroup of the XCD mapping (whole workgroup)
@@ -238,35 +256,40 @@ __global__ void __launch_bounds__(scalar_max_threads<W>()) scalar_kernel(const S
     const int H = static_cast<int>(a.shape & 0x1ffffu);
     const int ng = H / E;  // groups per row
     const int span = S * n;
-    const size_t base = static_cast<size_t>(row) * static_cast<size_t>(ng);
-    const int line_off = static_cast<int>(
-        (reinterpret_cast<uintptr_t>(static_cast<const G*>(a.x.p[0]) + base) & 127u) / sizeof(G));
-    const int shift = (ng <= span && ng + line_off > span) ? 0 : line_off;
-    const int nidx = ng + shift;  // lane indexes that cover the row
-    const G* res = static_cast<const G*>(a.residual) + base;
-    const G* w = static_cast<const G*>(a.weight);
-    G* ro_out = static_cast<G*>(a.residual_out) + base;
-    G* n_out = static_cast<G*>(a.norm_out) + base;
+    const int row_bytes = 2 * H;
+    const size_t base = static_cast<size_t>(row) * static_cast<size_t>(H);  // the row's first element
+    const uint16_t* x0 = static_cast<const uint16_t*>(a.x.p[0]) + base;
+    const int shift = static_cast<int>((reinterpret_cast<uintptr_t>(x0) & 127u) / sizeof(G));
+    const bool single = ng <= span;               // one span: rotate; longer rows: shift
+    const int nidx = single ? span : ng + shift;  // lane indexes that cover the row
+    const int first = tid - shift;                // group of the lane's first index
+    const int first_off = static_cast<int>(sizeof(G)) * ((single && first < 0) ? first + span : first);
+    // byte offset of the lane's u-th group in the span from index i0
+    auto offset = [=](int i0, int u) {
+        return (i0 == 0 && u == 0) ? first_off : static_cast<int>(sizeof(G)) * (i0 + u * n + first);
+    };
+    Rsrc rx[WL];
+#pragma unroll
+    for (int r = 0; r < WL; ++r) rx[r] = make_rsrc(static_cast<const uint16_t*>(a.x.p[r]) + base, row_bytes);
+    const Rsrc rres = make_rsrc(static_cast<const uint16_t*>(a.residual) + base, row_bytes);
+    const Rsrc rw = make_rsrc(a.weight, row_bytes);
+    const Rsrc rro = make_rsrc(static_cast<uint16_t*>(a.residual_out) + base, row_bytes);
+    const Rsrc rno = make_rsrc(static_cast<uint16_t*>(a.norm_out) + base, row_bytes);
 
     double ss = 0.0;
     G keep[S];  // residual_out of the last span
-    G wk[S];    // weight of the last span, loaded with its inputs (no branch between the loads)
-    // Ranks whose loads the span keeps in registers: all W of a specialised kernel;
-    // the generic kernel (up to 16 ranks, W known at run time) adds the ranks after
-    // x_0 one at a time instead, which keeps its registers within budget.
-    constexpr int WL = W > 0 ? W : 1;
+    G wk[S];    // weight of the last span, loaded with its inputs
     for (int i0 = 0; i0 < nidx; i0 += span) {
-        const int g0 = i0 - shift;  // group of the span's first index
         // every load of the span first (the ranks kept, residual, weight), then the arithmetic
         G xv[WL][S];
         G rs[S];
 #pragma unroll
         for (int u = 0; u < S; ++u) {
-            const int g = min(max(g0 + u * n + tid, 0), ng - 1);
+            const int off = offset(i0, u);
 #pragma unroll
-            for (int r = 0; r < WL; ++r) xv[r][u] = __builtin_nontemporal_load(static_cast<const G*>(a.x.p[r]) + base + g);
-            rs[u] = __builtin_nontemporal_load(res + g);
-            wk[u] = w[g];
+            for (int r = 0; r < WL; ++r) xv[r][u] = B::template ld<kBufNT>(rx[r], off);
+            rs[u] = B::template ld<kBufNT>(rres, off);
+            wk[u] = B::template ld<0>(rw, off);
         }
         // keep the scheduler from interleaving the arithmetic (and its waits) into the loads
         __builtin_amdgcn_sched_barrier(0);
@@ -282,11 +305,13 @@ __global__ void __launch_bounds__(scalar_max_threads<W>()) scalar_kernel(const S
             }
         }
         if constexpr (W == 0) {
+            // the generic kernel (up to 16 ranks, W known at run time) adds the ranks
+            // after x_0 one at a time, which keeps its registers within budget
             for (int r = 1; r < world; ++r) {
-                const G* xr = static_cast<const G*>(a.x.p[r]) + base;
+                const Rsrc rr = make_rsrc(static_cast<const uint16_t*>(a.x.p[r]) + base, row_bytes);
                 G v[S];
 #pragma unroll
-                for (int u = 0; u < S; ++u) v[u] = __builtin_nontemporal_load(xr + min(max(g0 + u * n + tid, 0), ng - 1));
+                for (int u = 0; u < S; ++u) v[u] = B::template ld<kBufNT>(rr, offset(i0, u));
 #pragma unroll
                 for (int u = 0; u < S; ++u)
 #pragma unroll
@@ -295,20 +320,18 @@ __global__ void __launch_bounds__(scalar_max_threads<W>()) scalar_kernel(const S
         }
 #pragma unroll
         for (int u = 0; u < S; ++u) {
-            const int g = g0 + u * n + tid;
             const G rg = pack<E>(acc[u]);
             float o[E];
 #pragma unroll
             for (int k = 0; k < E; ++k) o[k] = Group<E>::get(rg, k) + Group<E>::get(rs[u], k);
             const G og = pack<E>(o);
             keep[u] = og;
-            if (g >= 0 && g < ng) {
-                ro_out[g] = og;
+            B::template st<RC ? 0 : kBufNT>(og, rro, offset(i0, u));
 #pragma unroll
-                for (int k = 0; k < E; ++k) {
-                    const double d = static_cast<double>(Group<E>::get(og, k));
-                    ss = __builtin_fma(d, d, ss);
-                }
+            for (int k = 0; k < E; ++k) {
+                // zero outside the row (its loads returned zeros)
+                const double d = static_cast<double>(Group<E>::get(og, k));
+                ss = __builtin_fma(d, d, ss);
             }
         }
     }
@@ -320,33 +343,30 @@ __global__ void __launch_bounds__(scalar_max_threads<W>()) scalar_kernel(const S
     for (int i = 1; i < (n >> 6); ++i) total = total + wave_ss[i];
     const float inv = inv_rms(total, static_cast<double>(H), a.eps);
 
-    if (nidx <= span) {
+    if (single) {
 #pragma unroll
         for (int u = 0; u < S; ++u) {
-            const int g = u * n + tid - shift;
             float v[E];
 #pragma unroll
             for (int k = 0; k < E; ++k) v[k] = (Group<E>::get(keep[u], k) * inv) * Group<E>::get(wk[u], k);
-            if (g >= 0 && g < ng) __builtin_nontemporal_store(pack<E>(v), n_out + g);
+            B::template st<kBufNT>(pack<E>(v), rno, offset(0, u));
         }
         return;
     }
     for (int i0 = 0; i0 < nidx; i0 += span) {
-        const int g0 = i0 - shift;
         G rv[S], wv[S];
 #pragma unroll
         for (int u = 0; u < S; ++u) {
-            const int g = min(max(g0 + u * n + tid, 0), ng - 1);
-            rv[u] = ro_out[g];
-            wv[u] = w[g];
+            const int off = offset(i0, u);
+            rv[u] = B::template ld<0>(rro, off);
+            wv[u] = B::template ld<0>(rw, off);
         }
 #pragma unroll
         for (int u = 0; u < S; ++u) {
-            const int g = g0 + u * n + tid;
             float v[E];
 #pragma unroll
             for (int k = 0; k < E; ++k) v[k] = (Group<E>::get(rv[u], k) * inv) * Group<E>::get(wv[u], k);
-            if (g >= 0 && g < ng) __builtin_nontemporal_store(pack<E>(v), n_out + g);
+            B::template st<kBufNT>(pack<E>(v), rno, offset(i0, u));
         }
     }
 }
@@ -424,28 +444,28 @@ hipError_t launch_scalar_with(const void* fn, const Args& a, int grid, int block
 
 // Instantiated (W, VPT) pairs: those whose (W + 2) * VPT live vectors fit the
 // register budget the host planner allows (40); others are never planned.
-template <int VPT>
+template <int VPT, bool RC>
 const void* row_fn(int world) {
     if (VPT == 8 && world > 3) return nullptr;
     switch (world) {
-        case 1: return reinterpret_cast<const void*>(&row_kernel<1, VPT>);
-        case 2: return reinterpret_cast<const void*>(&row_kernel<2, VPT>);
-        case 3: return reinterpret_cast<const void*>(&row_kernel<3, VPT>);
+        case 1: return reinterpret_cast<const void*>(&row_kernel<1, VPT, RC>);
+        case 2: return reinterpret_cast<const void*>(&row_kernel<2, VPT, RC>);
+        case 3: return reinterpret_cast<const void*>(&row_kernel<3, VPT, RC>);
         default: break;
     }
     if constexpr (VPT <= 4) {
         switch (world) {
-            case 4: return reinterpret_cast<const void*>(&row_kernel<4, VPT>);
-            case 5: return reinterpret_cast<const void*>(&row_kernel<5, VPT>);
-            case 6: return reinterpret_cast<const void*>(&row_kernel<6, VPT>);
-            case 7: return reinterpret_cast<const void*>(&row_kernel<7, VPT>);
-            case 8: return reinterpret_cast<const void*>(&row_kernel<8, VPT>);
+            case 4: return reinterpret_cast<const void*>(&row_kernel<4, VPT, RC>);
+            case 5: return reinterpret_cast<const void*>(&row_kernel<5, VPT, RC>);
+            case 6: return reinterpret_cast<const void*>(&row_kernel<6, VPT, RC>);
+            case 7: return reinterpret_cast<const void*>(&row_kernel<7, VPT, RC>);
+            case 8: return reinterpret_cast<const void*>(&row_kernel<8, VPT, RC>);
             default: break;
         }
     }
     if constexpr (VPT <= 2) {
-        if (world == 16) return reinterpret_cast<const void*>(&row_kernel<16, VPT>);
-        return reinterpret_cast<const void*>(&row_kernel<0, VPT>);
+        if (world == 16) return reinterpret_cast<const void*>(&row_kernel<16, VPT, RC>);
+        return reinterpret_cast<const void*>(&row_kernel<0, VPT, RC>);
     }
     return nullptr;
 }
@@ -474,15 +494,16 @@ const void* splith_fn(int world) {
 
 hipError_t launch_row(const Args& a, int vpt, int grid, int block, hipStream_t s) {
     const void* fn = nullptr;
+    const bool rc = a.ro_cached != 0;
     switch (vpt) {
-        case 1: fn = row_fn<1>(a.world); break;
-        case 2: fn = row_fn<2>(a.world); break;
-        case 4: fn = row_fn<4>(a.world); break;
-        case 8: fn = row_fn<8>(a.world); break;
+        case 1: fn = rc ? row_fn<1, true>(a.world) : row_fn<1, false>(a.world); break;
+        case 2: fn = rc ? row_fn<2, true>(a.world) : row_fn<2, false>(a.world); break;
+        case 4: fn = rc ? row_fn<4, true>(a.world) : row_fn<4, false>(a.world); break;
+        case 8: fn = rc ? row_fn<8, true>(a.world) : row_fn<8, false>(a.world); break;
         default: return hipErrorInvalidValue;
     }
     if (!fn) return hipErrorInvalidValue;
-    // row_kernel<W, VPT> takes RowArgs<W> for W <= 8 and RowArgs<16> otherwise
+    // row_kernel<W, VPT, RC> takes RowArgs<W> for W <= 8 and RowArgs<16> otherwise
     switch (a.world) {
         case 1: return launch_row_with<1>(fn, a, grid, block, s);
         case 2: return launch_row_with<2>(fn, a, grid, block, s);
@@ -530,27 +551,28 @@ hipError_t launch_splith(const Args& a, int vpt, int grid, int block, hipStream_
     return launch_with(reinterpret_cast<const void*>(&splith_norm_kernel), n, grid, block, s);
 }
 
-template <int E>
+template <int E, bool RC>
 const void* scalar_fn(int world) {
     switch (world) {
-        case 1: return reinterpret_cast<const void*>(&scalar_kernel<1, E>);
-        case 2: return reinterpret_cast<const void*>(&scalar_kernel<2, E>);
-        case 3: return reinterpret_cast<const void*>(&scalar_kernel<3, E>);
-        case 4: return reinterpret_cast<const void*>(&scalar_kernel<4, E>);
-        case 5: return reinterpret_cast<const void*>(&scalar_kernel<5, E>);
-        case 6: return reinterpret_cast<const void*>(&scalar_kernel<6, E>);
-        case 7: return reinterpret_cast<const void*>(&scalar_kernel<7, E>);
-        case 8: return reinterpret_cast<const void*>(&scalar_kernel<8, E>);
-        default: return reinterpret_cast<const void*>(&scalar_kernel<0, E>);
+        case 1: return reinterpret_cast<const void*>(&scalar_kernel<1, E, RC>);
+        case 2: return reinterpret_cast<const void*>(&scalar_kernel<2, E, RC>);
+        case 3: return reinterpret_cast<const void*>(&scalar_kernel<3, E, RC>);
+        case 4: return reinterpret_cast<const void*>(&scalar_kernel<4, E, RC>);
+        case 5: return reinterpret_cast<const void*>(&scalar_kernel<5, E, RC>);
+        case 6: return reinterpret_cast<const void*>(&scalar_kernel<6, E, RC>);
+        case 7: return reinterpret_cast<const void*>(&scalar_kernel<7, E, RC>);
+        case 8: return reinterpret_cast<const void*>(&scalar_kernel<8, E, RC>);
+        default: return reinterpret_cast<const void*>(&scalar_kernel<0, E, RC>);
     }
 }
 
 hipError_t launch_scalar(const Args& a, int grid, int block, hipStream_t s) {
     const void* fn = nullptr;
+    const bool rc = a.ro_cached != 0;
     switch (a.elems_per_load) {
-        case 1: fn = scalar_fn<1>(a.world); break;
-        case 2: fn = scalar_fn<2>(a.world); break;
-        case 4: fn = scalar_fn<4>(a.world); break;
+        case 1: fn = rc ? scalar_fn<1, true>(a.world) : scalar_fn<1, false>(a.world); break;
+        case 2: fn = rc ? scalar_fn<2, true>(a.world) : scalar_fn<2, false>(a.world); break;
+        case 4: fn = rc ? scalar_fn<4, true>(a.world) : scalar_fn<4, false>(a.world); break;
         default: return hipErrorInvalidValue;
     }
     switch (a.world) {

@@ -48,7 +48,10 @@ int main(int argc, char** argv) {
         const int maxt = (next() % 4) ? (int)(next() % 20000) : 0x7fffffff;
         const int cu = (next() % 8) ? 256 : (int)(next() % 300);
         const int trpb[] = {0, 0, 0, 1, 2, 3, 4, 8, 64, 128};
-        arrms_tuning_t tun = {pick(tvpt, 8), pick(ttpr, 13), pick(tblk, 7), pick(tspl, 6), pick(txcd, 8), pick(trpb, 10)};
+        const int tse[] = {0, 0, 1, 2, 4, 3};
+        const int tro[] = {0, 0, 0, 1, 2, 3, -1};
+        arrms_tuning_t tun = {pick(tvpt, 8), pick(ttpr, 13), pick(tblk, 7), pick(tspl, 6), pick(txcd, 8), pick(trpb, 10),
+                              pick(tse, 6), pick(tro, 7)};
         const arrms_tuning_t* tp = (next() % 3) ? &tun : nullptr;
         const int variant = (int)(next() % 6) - 1;
         const uintptr_t base = 0x7f0000000000ull;
@@ -86,7 +89,17 @@ int main(int argc, char** argv) {
                 return fail("variant", i);
             }
             if (p.xcd_chunk && p.grid % (8 * p.xcd_chunk)) return fail("xcd grid", i);
+            // residual_out store policy: split-H always write-back (read back by its second
+            // kernel); row and scalar follow a tuned policy, else write-back up to 128 MiB of
+            // residual_out per call (from 24 MiB with one or two ranks)
+            const long long ro_bytes = 2LL * T * H;
+            int want = (ro_bytes <= (128LL << 20) && !(W <= 2 && ro_bytes < (24LL << 20))) ? 1 : 0;
+            if (tp && tp->residual_out_store) want = tp->residual_out_store == 2;
+            if (p.variant == ARRMS_VARIANT_SPLITH) want = 1;
+            if (p.residual_out_cached != want) return fail("residual_out store policy", i);
         }
+        if (rc == ARRMS_OK && tp && (tp->residual_out_store < 0 || tp->residual_out_store > 2 || tp->scalar_elems == 3))
+            return fail("invalid tuning accepted", i);
         // The no-allocation entry point's plan (automatic, no tuning, absolute limits):
         // every plan it accepts keeps the split-H workspace index, row * chunks + chunk
         // for row < T, inside its static scratch.

@@ -395,6 +395,46 @@ def test_scalar_load_width_tuning_and_vector_plans():
     assert plan(4, 64, 2044, tuning=A.arrms_tuning_t.make(scalar_elems=3))[0] == A.ARRMS_ERR_INVALID_ARG
 
 
+# residual_out store policy of the row and scalar kernels: write-back stores while a call
+# writes at most 128 MiB of residual_out, from 24 MiB with one or two ranks; split-H always
+# writes back (its second kernel reads residual_out again).
+@pytest.mark.parametrize("W,T,H,variant,cached", [
+    (4, 4096, 2048, A.ARRMS_VARIANT_ROW, 1),      # 16 MiB
+    (3, 2048, 2048, A.ARRMS_VARIANT_ROW, 1),      # 8 MiB, three ranks
+    (2, 4096, 2048, A.ARRMS_VARIANT_ROW, 0),      # 16 MiB, two ranks
+    (2, 6143, 2048, A.ARRMS_VARIANT_ROW, 0),      # just under 24 MiB
+    (2, 6144, 2048, A.ARRMS_VARIANT_ROW, 1),      # 24 MiB
+    (1, 6144, 2048, A.ARRMS_VARIANT_ROW, 1),
+    (4, 16384, 4096, A.ARRMS_VARIANT_ROW, 1),     # 128 MiB
+    (4, 16385, 4096, A.ARRMS_VARIANT_ROW, 0),     # just over
+    (8, 16383, 5120, A.ARRMS_VARIANT_ROW, 0),     # 160 MiB
+    (16, 4096, 2048, A.ARRMS_VARIANT_ROW, 1),
+    (4, 4096, 2047, A.ARRMS_VARIANT_SCALAR, 1),
+    (8, 16383, 5119, A.ARRMS_VARIANT_SCALAR, 0),
+    (2, 100, 2046, A.ARRMS_VARIANT_SCALAR, 0),
+    (8, 1, 8192, A.ARRMS_VARIANT_SPLITH, 1),
+    (4, 16, 16384, A.ARRMS_VARIANT_SPLITH, 1),
+])
+def test_residual_out_store_policy(W, T, H, variant, cached):
+    rc, p = plan(W, T, H)
+    assert rc == A.ARRMS_OK and p["variant"] == variant, p
+    assert p["residual_out_cached"] == cached
+
+
+def test_residual_out_store_tuning():
+    for store, want in ((1, 0), (2, 1)):
+        t = A.arrms_tuning_t.make(residual_out_store=store)
+        for W, T, H in ((4, 4096, 2048), (8, 16383, 5120), (4, 64, 2047), (2, 16, 2048)):
+            rc, p = plan(W, T, H, tuning=t)
+            assert rc == A.ARRMS_OK and p["residual_out_cached"] == want, (W, T, H, p)
+        rc, p = plan(8, 1, 8192, tuning=t)                        # split-H reads it back: always write-back
+        assert p["variant"] == A.ARRMS_VARIANT_SPLITH and p["residual_out_cached"] == 1
+    for bad in (-1, 3):
+        assert plan(4, 64, 2048, tuning=A.arrms_tuning_t.make(residual_out_store=bad))[0] == A.ARRMS_ERR_INVALID_ARG
+    rc, p = rplan(4, 16, 2048)
+    assert rc == A.ARRMS_OK and p["residual_out_cached"] == 0    # the rank sum writes no residual_out
+
+
 def test_tuned_rows_per_block_keeps_one_vector_layout():
     """Tuning only the rows per workgroup is a layout override: the automatic four-vector
     layout (16 lanes per row at H=512) is not taken, so the row kernel still runs."""

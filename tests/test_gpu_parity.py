@@ -97,8 +97,7 @@ SCALAR_SPANS = [(4, 5, 1, False), (3, 7, 3, False), (4, 9, 8191, False), (4, 9, 
 def test_scalar_spans(W, T, H, inplace):
     plan, _ = parity(W, T, H, variant=SCALAR, inplace=inplace, seed=H)
     assert plan["variant"] == SCALAR
-    lines = H % 64 == 0  # the partials start on 128-byte lines: no room needed for a line shift
-    assert plan["block"] == min(512 if W > 8 else 1024, -(-(-(-(H + (0 if lines else 63)) // 8)) // 64) * 64)
+    assert plan["block"] == min(512 if W > 8 else 1024, -(-(-(-H // 8)) // 64) * 64)
 
 
 # The scalar variant loads 4, 2 or 1 BF16 elements at a time: the widest that H and
@@ -115,6 +114,16 @@ SCALAR_WIDTHS = [
     (2, 17, 24580, 8, "all", 4), (11, 29, 4092, 0, "all", 4), (16, 7, 6146, 4, "all", 2),
     (1, 1000, 2044, 0, "all", 4), (1, 3, 1, 0, "all", 1),
 ]
+
+
+# Both residual_out store policies (streaming and write-back stores) on the row and the
+# scalar kernels: the same bits either way, in one span and in several.
+@pytest.mark.parametrize("W,T,H,variant", [(4, 130, 2048, ROW), (2, 33, 1000, ROW), (4, 130, 2047, SCALAR),
+                                           (3, 9, 8193, SCALAR), (12, 17, 4096, ROW), (9, 5, 1001, SCALAR)])
+@pytest.mark.parametrize("store", [1, 2])
+def test_residual_out_store_policies(W, T, H, variant, store):
+    plan, _ = parity(W, T, H, variant=variant, tuning=dict(residual_out_store=store), seed=T + H + store)
+    assert plan["residual_out_cached"] == store - 1
 
 
 def _shifted(t, off, dev):
