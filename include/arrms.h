@@ -90,13 +90,15 @@ typedef struct {
  * None of them changes any result bit, only speed. */
 typedef struct {
     int vec_per_thread;    /* row / split-H: 1, 2, 4 or 8 */
-    int threads_per_row;   /* row: 16, 32 or a multiple of 64 up to 1024 */
+    int threads_per_row;   /* row: 16, 32 or a multiple of 64 up to 1024; scalar: lanes per row when a multiple
+                              of 64 (capped at 1024, or 512 for more than 8 ranks) */
     int splith_block;      /* split-H: threads per workgroup, 64..1024, multiple of 64 */
     int splith_max_tokens; /* automatic variant uses split-H when tokens <= this; -1 automatic */
     int xcd_chunk;         /* -1 automatic; 0 hardware round-robin; K > 0 runs of K blocks per XCD */
     int rows_per_block;    /* row: token rows per workgroup (power of two); 0 automatic */
     int scalar_elems;      /* scalar and rank sum: at most this many BF16 elements per load (1, 2 or 4); 0 automatic */
-    int residual_out_store; /* row and scalar: 0 automatic, 1 streaming stores, 2 write-back stores */
+    int residual_out_store; /* row and scalar: 0 or 1 streaming stores (automatic), 2 write-back stores (faster
+                               only when the call's data is cache-resident) */
 } arrms_tuning_t;
 
 /*

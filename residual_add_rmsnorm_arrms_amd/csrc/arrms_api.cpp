@@ -46,16 +46,14 @@ constexpr long kXcdRunBytes = 3L << 20;
 constexpr int kReduceAutoVpt = 1;
 // Rows with less traffic than this never use split-H automatically.
 constexpr long kSplitMinRowBytes = 144L << 10;
-// Store policy of residual_out in the row and scalar kernels (measured on MI355X
-// with the row kernel over 87 shapes, W = 1..16, H = 1024..16384, T = 2048..16384,
-// back-to-back calls on buffers beyond the Infinity Cache): write-back stores beat
-// streaming ones by 2-9 % while a call writes at most 128 MiB of residual_out, half
-// the 256 MB Infinity Cache, and lose up to 11 % above it; with one or two ranks
-// they also lose, up to 12 %, below 24 MiB (those calls run four rows per
-// workgroup).  The rule below is never more than 2.3 % slower than streaming stores
-// on any measured shape (W = 8 and 16 at 16-32 MiB lose 1-2.3 %).
-constexpr long long kRoCachedMaxBytes = 128LL << 20;
-constexpr long long kRoCachedFewRanksMinBytes = 24LL << 20;
+// Store policy of residual_out in the row and scalar kernels: streaming
+// (non-temporal) stores unless tuned.  Measured on MI355X with back-to-back calls
+// rotating over 4.5 GB of buffers, write-back stores were 3-9 % slower on most
+// shapes (W = 1..16, H = 1024..16384, T = 1024..16384) and at most 2 % faster on a
+// few small ones; with a rotation of only 0.7 GB (partly served by the Infinity
+// Cache) they were 2-9 % faster up to 128 MiB of residual_out per call.  So
+// write-back stores pay only where the call's data is cache-resident; the tuning
+// field selects them for such callers.
 
 int chunks_capacity(int max_hidden) {
     const int nvec = (max_hidden + 7) / 8;
@@ -103,13 +101,7 @@ bool valid_tuning(const arrms_tuning_t* t) {
 }
 
 // Write-back (1) or streaming (0) stores for residual_out in the row and scalar kernels.
-int residual_out_cached(int world, int tokens, int hidden, const arrms_tuning_t* t) {
-    if (t && t->residual_out_store) return t->residual_out_store == 2;
-    const long long bytes = 2LL * tokens * hidden;
-    if (bytes > kRoCachedMaxBytes) return 0;
-    if (world <= 2 && bytes < kRoCachedFewRanksMinBytes) return 0;
-    return 1;
-}
+int residual_out_cached(const arrms_tuning_t* t) { return t && t->residual_out_store == 2; }
 
 // Launch shape of a vector-variant plan whose logical workgroup count is
 // p->blocks.  The XCD mapping keeps runs of K consecutive blocks on one XCD
@@ -188,7 +180,7 @@ int plan_row(int cu_count, int world, int tokens, int hidden, const arrms_tuning
     p->block = best_tpr * rpb;
     p->blocks = static_cast<int>((static_cast<long>(tokens) + rpb - 1) / rpb);
     p->kernels = 1;
-    p->residual_out_cached = residual_out_cached(world, tokens, hidden, t);
+    p->residual_out_cached = residual_out_cached(t);
     // Automatic XCD runs: about 3 MiB of traffic per run, a power of two of
     // blocks (measured best: 64 blocks at W=4 H=2048, 16 at W=8 H=5120/8192);
     // small grids keep the hardware order.
@@ -251,7 +243,7 @@ int plan_splith(int cu_count, int max_hidden, int world, int tokens, int hidden,
 
 // Scalar plan: one row per workgroup, 8 elements per lane per span: enough whole
 // waves to cover the row in one span, at most 1024 lanes (512 for more than 8
-// ranks: the kernels' __launch_bounds__).  Loads are `elems` BF16
+// ranks: the kernels' __launch_bounds__); a longer row runs on 256 lanes.  Loads are `elems` BF16
 // elements wide (the widest that H and every pointer's alignment allow, at most
 // the tuned width).  XCD runs as in the row variant (about 3 MiB of traffic per run).
 // The kernel aligns its lanes to 128-byte lines by rotating a one-span row, so a
@@ -259,6 +251,11 @@ int plan_splith(int cu_count, int max_hidden, int world, int tokens, int hidden,
 void plan_scalar(int world, int tokens, int hidden, int elems, const arrms_tuning_t* t, arrms_plan_t* p) {
     const int max_block = world > 8 ? 512 : 1024;
     int block = ((hidden + 7) / 8 + 63) / 64 * 64;
+    // A row longer than one span of the largest workgroup takes several spans anyway;
+    // 4-wave workgroups run them 9-13 % faster than the largest ones (measured on
+    // MI355X at W=4 and W=1 with H=16383, and W=16 with H=5119).
+    if (block > max_block) block = 256;
+    if (t && t->threads_per_row >= 64) block = t->threads_per_row;  // tuned: a multiple of 64
     if (block > max_block) block = max_block;
     if (t && t->scalar_elems && t->scalar_elems < elems) elems = t->scalar_elems;
     p->variant = ARRMS_VARIANT_SCALAR;
@@ -270,7 +267,7 @@ void plan_scalar(int world, int tokens, int hidden, int elems, const arrms_tunin
     p->blocks = tokens;
     p->kernels = 1;
     p->elems_per_load = elems;
-    p->residual_out_cached = residual_out_cached(world, tokens, hidden, t);
+    p->residual_out_cached = residual_out_cached(t);
     int k = 0;
     if (p->blocks >= 64) {
         const long row_bytes = 2L * (world + 3) * hidden;

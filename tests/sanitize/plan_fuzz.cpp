@@ -83,18 +83,18 @@ int main(int argc, char** argv) {
                 uintptr_t any = (uintptr_t)res | (uintptr_t)w | (uintptr_t)ro | (uintptr_t)no;
                 for (int r = 0; r < W; ++r) any |= (uintptr_t)parts[r];
                 if (any & (uintptr_t)(2 * e - 1)) return fail("scalar load alignment", i);
-                if ((long)p.block * 8 < H && p.block != (W > 8 ? 512 : 1024)) return fail("scalar span", i);
+                const bool tuned_block = tp && tp->threads_per_row >= 64;
+                if (!tuned_block && (long)p.block * 8 < H && p.block != 256) return fail("scalar span", i);
+                if (!tuned_block && (long)p.block * 8 >= H && (long)(p.block - 64) * 8 >= H)
+                    return fail("scalar lanes", i);
                 if (p.block > (W > 8 ? 512 : 1024)) return fail("scalar block", i);
             } else {
                 return fail("variant", i);
             }
             if (p.xcd_chunk && p.grid % (8 * p.xcd_chunk)) return fail("xcd grid", i);
             // residual_out store policy: split-H always write-back (read back by its second
-            // kernel); row and scalar follow a tuned policy, else write-back up to 128 MiB of
-            // residual_out per call (from 24 MiB with one or two ranks)
-            const long long ro_bytes = 2LL * T * H;
-            int want = (ro_bytes <= (128LL << 20) && !(W <= 2 && ro_bytes < (24LL << 20))) ? 1 : 0;
-            if (tp && tp->residual_out_store) want = tp->residual_out_store == 2;
+            // kernel); row and scalar streaming unless tuned to write-back
+            int want = tp && tp->residual_out_store == 2;
             if (p.variant == ARRMS_VARIANT_SPLITH) want = 1;
             if (p.residual_out_cached != want) return fail("residual_out store policy", i);
         }

@@ -395,23 +395,14 @@ def test_scalar_load_width_tuning_and_vector_plans():
     assert plan(4, 64, 2044, tuning=A.arrms_tuning_t.make(scalar_elems=3))[0] == A.ARRMS_ERR_INVALID_ARG
 
 
-# residual_out store policy of the row and scalar kernels: write-back stores while a call
-# writes at most 128 MiB of residual_out, from 24 MiB with one or two ranks; split-H always
-# writes back (its second kernel reads residual_out again).
+# residual_out store policy: the row and scalar kernels stream it (non-temporal stores)
+# unless tuned; split-H always writes it back (its second kernel reads residual_out again).
 @pytest.mark.parametrize("W,T,H,variant,cached", [
-    (4, 4096, 2048, A.ARRMS_VARIANT_ROW, 1),      # 16 MiB
-    (3, 2048, 2048, A.ARRMS_VARIANT_ROW, 1),      # 8 MiB, three ranks
-    (2, 4096, 2048, A.ARRMS_VARIANT_ROW, 0),      # 16 MiB, two ranks
-    (2, 6143, 2048, A.ARRMS_VARIANT_ROW, 0),      # just under 24 MiB
-    (2, 6144, 2048, A.ARRMS_VARIANT_ROW, 1),      # 24 MiB
-    (1, 6144, 2048, A.ARRMS_VARIANT_ROW, 1),
-    (4, 16384, 4096, A.ARRMS_VARIANT_ROW, 1),     # 128 MiB
-    (4, 16385, 4096, A.ARRMS_VARIANT_ROW, 0),     # just over
-    (8, 16383, 5120, A.ARRMS_VARIANT_ROW, 0),     # 160 MiB
-    (16, 4096, 2048, A.ARRMS_VARIANT_ROW, 1),
-    (4, 4096, 2047, A.ARRMS_VARIANT_SCALAR, 1),
+    (4, 4096, 2048, A.ARRMS_VARIANT_ROW, 0),
+    (2, 6144, 2048, A.ARRMS_VARIANT_ROW, 0),
+    (8, 16383, 5120, A.ARRMS_VARIANT_ROW, 0),
+    (4, 4096, 2047, A.ARRMS_VARIANT_SCALAR, 0),
     (8, 16383, 5119, A.ARRMS_VARIANT_SCALAR, 0),
-    (2, 100, 2046, A.ARRMS_VARIANT_SCALAR, 0),
     (8, 1, 8192, A.ARRMS_VARIANT_SPLITH, 1),
     (4, 16, 16384, A.ARRMS_VARIANT_SPLITH, 1),
 ])
@@ -419,6 +410,15 @@ def test_residual_out_store_policy(W, T, H, variant, cached):
     rc, p = plan(W, T, H)
     assert rc == A.ARRMS_OK and p["variant"] == variant, p
     assert p["residual_out_cached"] == cached
+
+
+def test_scalar_lanes_tuning():
+    """threads_per_row sets the scalar kernel's lanes per row when it is a multiple of 64."""
+    for tpr, want in ((256, 256), (512, 512), (64, 64), (1024, 1024), (32, 640)):
+        rc, p = plan(8, 100, 5119, tuning=A.arrms_tuning_t.make(threads_per_row=tpr))
+        assert rc == A.ARRMS_OK and p["variant"] == A.ARRMS_VARIANT_SCALAR and p["block"] == want, (tpr, p)
+    rc, p = plan(12, 100, 5119, tuning=A.arrms_tuning_t.make(threads_per_row=1024))   # > 8 ranks: at most 512
+    assert p["block"] == 512
 
 
 def test_residual_out_store_tuning():
