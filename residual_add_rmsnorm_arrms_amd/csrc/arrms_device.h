@@ -130,6 +130,16 @@ template <> struct Buf<4> {
     }
 };
 
+template <> struct Buf<8> {
+    typedef decltype(__builtin_amdgcn_raw_buffer_load_b128(Rsrc(), 0, 0, 0)) Raw;
+    template <int AUX> static __device__ __forceinline__ u32x4 ld(Rsrc r, int off) {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+    }
+    template <int AUX> static __device__ __forceinline__ void st(u32x4 v, Rsrc r, int off) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(Raw, v), r, off, 0, AUX);
+    }
+};
+
 // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on XCD
 // b % 8).  With xcd_chunk = K > 0 the launched grid is a multiple of 8K and
 // the i-th workgroup an XCD receives takes logical block (8 * (i / K) + x) * K

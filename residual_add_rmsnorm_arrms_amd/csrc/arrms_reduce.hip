@@ -26,56 +26,54 @@ constexpr int kReduceLanes = 256;
 // partial, all loads issued first; the last workgroup adds the `head` elements
 // before the aligned start and the count % E after the last whole group, element
 // by element.
+// Each workgroup reaches its groups through buffer resources that span exactly
+// its own whole groups of each tensor: the hardware's range check returns zeros
+// for a load past them and drops such a store, so no group index is clamped or
+// branched on, and one 32-bit offset per group serves every tensor.
 template <int W, int L, int E>
 __global__ void __launch_bounds__(kReduceLanes) reduce_kernel(const ReduceArgs<(W > 0 ? W : kMaxWorld)> a) {
     typedef typename Group<E>::T G;
+    typedef Buf<E> B;
     constexpr int WA = W > 0 ? W : kMaxWorld;
     const int world = W > 0 ? W : a.world;
     const int block = logical_block(a.xcd_chunk, a.blocks);
     if (block < 0) return;
-    const size_t ng = static_cast<size_t>(a.count) / E;
-    const size_t first = static_cast<size_t>(block) * kReduceLanes * L + threadIdx.x;
-    bool ok[L];
-    G xv[L][WA];
-    if (ng > 0) {  // (a call of fewer elements than one group has only its head and tail)
+    const long long ng = a.count / E;  // whole groups from the aligned start
+    const long long g0 = static_cast<long long>(block) * kReduceLanes * L;
+    if (g0 < ng) {  // (a call of fewer elements than one group has only its head and tail)
+        const long long span = ng - g0 < kReduceLanes * L ? ng - g0 : kReduceLanes * L;
+        const int bytes = static_cast<int>(span) * static_cast<int>(sizeof(G));
+        const size_t first = static_cast<size_t>(g0) * E;  // the workgroup's first element
+        G xv[L][WA];
+        // rank by rank, so that each rank's resource lives only while its loads issue
 #pragma unroll
-        for (int k = 0; k < L; ++k) {
-            const size_t g = first + static_cast<size_t>(k) * kReduceLanes;
-            ok[k] = g < ng;
-            if constexpr (E < 8 && W > 0) {
-                // Narrow loads: from a clamped index where the group lies past the end (its
-                // value is never used), so no branch separates the loads and all of them
-                // issue before the first wait.
-                const size_t gc = g < ng ? g : ng - 1;
+        for (int r = 0; r < WA; ++r) {
+            if (W > 0 || r < world) {
+                const Rsrc rx = make_rsrc(static_cast<const uint16_t*>(a.x.p[r]) + first, bytes);
 #pragma unroll
-                for (int r = 0; r < WA; ++r)
-                    xv[k][r] = __builtin_nontemporal_load(static_cast<const G*>(a.x.p[r]) + gc);
-            } else if (ok[k]) {
-#pragma unroll
-                for (int r = 0; r < WA; ++r)
-                    if (W > 0 || r < world)
-                        xv[k][r] = __builtin_nontemporal_load(static_cast<const G*>(a.x.p[r]) + g);
+                for (int k = 0; k < L; ++k)
+                    xv[k][r] = B::template ld<kBufNT>(
+                        rx, (k * kReduceLanes + static_cast<int>(threadIdx.x)) * static_cast<int>(sizeof(G)));
             }
         }
+        const Rsrc rout = make_rsrc(static_cast<uint16_t*>(a.reduced) + first, bytes);
 #pragma unroll
         for (int k = 0; k < L; ++k) {
-            if (ok[k]) {
-                float sum[E];
+            const int off = (k * kReduceLanes + static_cast<int>(threadIdx.x)) * static_cast<int>(sizeof(G));
+            float sum[E];
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    float acc = Group<E>::get(xv[k][0], e);
+            for (int e = 0; e < E; ++e) {
+                float acc = Group<E>::get(xv[k][0], e);
 #pragma unroll
-                    for (int r = 1; r < WA; ++r)
-                        if (W > 0 || r < world) acc = acc + Group<E>::get(xv[k][r], e);
-                    sum[e] = acc;
-                }
-                __builtin_nontemporal_store(pack<E>(sum),
-                                            static_cast<G*>(a.reduced) + first + static_cast<size_t>(k) * kReduceLanes);
+                for (int r = 1; r < WA; ++r)
+                    if (W > 0 || r < world) acc = acc + Group<E>::get(xv[k][r], e);
+                sum[e] = acc;
             }
+            B::template st<kBufNT>(pack<E>(sum), rout, off);
         }
     }
     if (block == a.blocks - 1) {  // the head and the tail, element-wise
-        const long long tail0 = static_cast<long long>(ng) * E;
+        const long long tail0 = ng * E;
         const int extra = a.head + static_cast<int>(a.count - tail0);
         for (int j = threadIdx.x; j < extra; j += kReduceLanes) {
             const long long e = j < a.head ? static_cast<long long>(j - a.head) : tail0 + (j - a.head);
