@@ -38,7 +38,9 @@ using namespace dev;
 // per workgroup.  Lane l handles vectors l, l + tpr, ..., l + (VPT-1)*tpr of the
 // row, so at each step a wave reads 1 KiB of contiguous memory per input.  All
 // (W + 2) * VPT loads of a lane are issued before any arithmetic; residual_out
-// stays in registers for the second pass.
+// stays in registers for the second pass.  Both outputs are written with
+// streaming stores, or residual_out with write-back stores when RC is set (a
+// tuning choice that pays only where the call's data stays cache-resident).
 // Largest workgroup of a row kernel; the host planner uses the same table.
 template <int W, int VPT>
 constexpr int row_max_threads() {
