@@ -628,6 +628,34 @@ def forced_variants(ctx):
     return variants
 
 
+def store_policy(ctx, tokens=(4096, 16384), rounds=2):
+    """residual_out written with streaming stores (the default) against write-back stores
+    (tuning residual_out_store=2) on the prefill pool's rotating buffers: back-to-back GPU
+    time, the two policies interleaved, the best of `rounds` each."""
+    torch, A, op = ctx.torch, ctx.A, ctx.op
+    out = []
+    for t in tokens:
+        best = {}
+        for _ in range(rounds):
+            for store, name in ((1, "streaming"), (2, "write_back")):
+                op.set_tuning(residual_out_store=store)
+                c = ctx.caller(t)
+                for _ in range(30):
+                    c()
+                _, g = time_back_to_back(torch, c, 300 if t <= 4096 else 100)
+                best[name] = min(best.get(name, 1e9), g * 1e3)
+        op.set_tuning()
+        b = algorithmic_bytes(ctx.W, t, ctx.H)
+        rec = {"W": ctx.W, "T": t, "H": ctx.H}
+        for name, us in best.items():
+            rec[name + "_us"] = us
+            rec[name + "_frac_of_peak_gpu_events"] = b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
+        out.append(rec)
+        log("residual_out stores W=%d T=%d H=%d: streaming %.2f us, write-back %.2f us" % (
+            ctx.W, t, ctx.H, best["streaming"], best["write_back"]))
+    return out
+
+
 def reduce_offsets(ctx, W=4, T=4096):
     """The rank sum alone at W=4 T=4096 H=2048 with its tensors placed at byte offsets:
     every tensor at the same offset (16-byte loads after a short head) and the output
@@ -1087,7 +1115,7 @@ def main():
         log("parity of the timed configuration vs oracle: %s" % parity)
 
     sweep, fit, fusion, reduce_sweep, variants, splith_regime, worlds = [], None, None, [], [], [], []
-    ceiling, scalar, reduce_offs = None, [], []
+    ceiling, scalar, reduce_offs, stores = None, [], [], []
     if not args.no_sweep:
         ctx = Ctx(torch, A, synth, op, pool, W, H, eps, stream)
         ceiling = read_ceiling(ctx, achieved)
@@ -1097,6 +1125,7 @@ def main():
         variants = forced_variants(ctx)
         scalar = scalar_widths(ctx)
         reduce_offs = reduce_offsets(ctx)
+        stores = store_policy(ctx, tokens=tuple(t for t in (4096, 16384) if t <= pool.T))
         splith_regime = splith_crossover(ctx)
         worlds = world_sweep(ctx)
 
@@ -1157,6 +1186,7 @@ def main():
         "variants": variants,
         "scalar_widths": scalar,
         "reduce_offsets": reduce_offs,
+        "store_policy": stores,
         "splith_regime": splith_regime,
         "world_sweep": worlds,
         "ceiling": ceiling,
