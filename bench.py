@@ -15,8 +15,9 @@ pool of distinct input/output sets (10 slots of 16384 rows; far more than the
 T = 4096, 8192, 16384 (beyond the metric's range) separate the per-call fixed time
 from the kernel's streaming rate.
 
-`--workload large_hidden` (W=8 T=8192 H=8192) or `--workload ragged_outliers`
-(W=8 T=16383 H=5120, 1% outliers) times those shapes instead, headline only.  Any
+`--workload large_hidden` (W=8 T=8192 H=8192), `--workload ragged_outliers`
+(W=8 T=16383 H=5120, 1% outliers) or `--workload odd_rows` (W=4 T=4096 H=2047, the
+scalar kernel's path) times those shapes instead, headline only.  Any
 shape can be timed the same way (rotating pool, oracle parity check, CPU baseline,
 JSON) with `--world/--tokens/--hidden/--eps/--x-sigma/--outlier-p/--seed`, which
 replace the named workload's values (the page's harness, section Implementation 6,
@@ -57,7 +58,7 @@ POOL_SLOTS = 10
 KERNEL_SRC = [os.path.join(ROOT, "residual_add_rmsnorm_arrms_amd", "csrc", f)
               for f in ("arrms_device.h", "arrms_kernels.hip", "arrms_api.cpp", "arrms_internal.h")]
 # workloads the benchmark can time (--workload); the default is the metric's own
-BENCH_WORKLOADS = ("prefill", "large_hidden", "ragged_outliers")
+BENCH_WORKLOADS = ("prefill", "large_hidden", "ragged_outliers", "odd_rows")
 
 
 def traffic_file(wl) -> str:
@@ -880,7 +881,7 @@ def read_counters(path: str) -> dict:
 
 
 def summarize_profiles(run_dir: str, workload: str, out_dir: str = None) -> None:
-    """Write profiles/row_kernel_<workload>.md and profiles/traffic_<workload>.json from
+    """Write profiles/<kernel>_<workload>.md and profiles/traffic_<workload>.json from
     the rocprofv3 outputs found under run_dir: bench.json and prof_bench/ (kernel trace of
     the benchmark command), pmc_<pass>/ for the counter passes of PMC_PASSES."""
     import collections
@@ -1002,7 +1003,7 @@ def summarize_profiles(run_dir: str, workload: str, out_dir: str = None) -> None
               "| mean read requests in flight per TCC channel, over its busy cycles | %.1f |" %
               stalls["mean_read_requests_in_flight_per_channel"],
               "| mean TCC-to-memory read latency, cycles | %.0f |" % stalls["mean_read_latency_cycles"]]
-    with open(os.path.join(out_dir, "row_kernel_%s.md" % base), "w") as f:
+    with open(os.path.join(out_dir, "%s_%s.md" % (kname.split("<")[0], base)), "w") as f:
         f.write("\n".join(L) + "\n")
 
 

@@ -109,7 +109,8 @@ class Workload:
 
 # The named workloads.  Shapes: tiny W=2 T=4 H=128; decode W=4 H=2048 T in {1,16,128};
 # prefill W=4 H=2048 T=4096 with partials ~N(0, 0.5^2); large hidden W=8 H=8192 T=8192, eps 1e-5;
-# ragged + outliers W=8 H=5120 T=16383, 1% of partial entries scaled by 100.
+# ragged + outliers W=8 H=5120 T=16383, 1% of partial entries scaled by 100; odd rows: the
+# prefill shape with H=2047 (rows the 16-byte kernels cannot take, for the scalar kernel's profile).
 WORKLOADS = {
     "tiny": Workload("tiny", 2, 4, 128),
     "decode_t1": Workload("decode_t1", 4, 1, 2048),
@@ -118,6 +119,7 @@ WORKLOADS = {
     "prefill": Workload("prefill", 4, 4096, 2048, x_sigma=0.5),
     "large_hidden": Workload("large_hidden", 8, 8192, 8192, eps=1e-5),
     "ragged_outliers": Workload("ragged_outliers", 8, 16383, 5120, outlier_p=0.01),
+    "odd_rows": Workload("odd_rows", 4, 4096, 2047, x_sigma=0.5),
 }
 
 
