@@ -277,6 +277,24 @@ void plan_scalar(int world, int tokens, int hidden, int elems, const arrms_tunin
     finish_vector_plan(t, p, k);
 }
 
+// More than 8 ranks: the automatic choice takes the scalar kernel for rows of one
+// span (H <= 4096 on its 512 lanes) once there are enough rows to overlap its rank
+// loop.  That kernel keeps only x_0, the residual and the weight in registers and adds
+// the other ranks one load round at a time, so it runs many more workgroups per CU
+// than the row kernel holding all 9-16 ranks; per row it pays one memory round trip
+// per rank.  Measured on MI355X (4.5 GB rotation) against the row kernel: 8-30 %
+// faster from T = 1024 at W = 9, 10, 12 and H = 2048-4096 (the generic 9-15-rank row
+// kernel), and 7-10 % faster from T = 2048 at W = 16 (its own row instance), but
+// 8 % slower at W = 16 T = 1024 and 1.3-2.3x slower at T <= 512.  Rows over 4096
+// elements (split-H or several scalar spans) measured even, so they keep their plan;
+// a tuned lane layout keeps the row kernel.
+bool many_ranks_scalar(int cu_count, int world, int tokens, int hidden, const arrms_tuning_t* t) {
+    if (world <= 8 || hidden > 8 * 512) return false;
+    if (t && (t->vec_per_thread || t->threads_per_row || t->rows_per_block)) return false;
+    const long long min_rows = static_cast<long long>(world == 16 ? 8 : 4) * cu_count;
+    return tokens >= min_rows;
+}
+
 // Widest load, in BF16 elements, that H and the OR of all pointer addresses allow.
 int scalar_elems(int hidden, uintptr_t any) {
     if (hidden % 4 == 0 && (any & 7u) == 0) return 4;
@@ -391,6 +409,11 @@ int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
     }
     int split_max = (tuning && tuning->splith_max_tokens >= 0) ? tuning->splith_max_tokens
                                                               : auto_splith_max_tokens(cu_count, world, hidden);
+    // More than 8 ranks, rows of one scalar span, enough rows: the scalar kernel.
+    if (tokens > split_max && many_ranks_scalar(cu_count, world, tokens, hidden, tuning)) {
+        plan_scalar(world, tokens, hidden, elems, tuning, plan);
+        return ARRMS_OK;
+    }
     // The automatic choice always finds a plan: tuning overrides that no vector
     // kernel can honour end in the scalar kernel (same results).
     if (hidden > ARRMS_ROW_MAX_HIDDEN || tokens <= split_max) {

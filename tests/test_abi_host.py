@@ -412,6 +412,34 @@ def test_residual_out_store_policy(W, T, H, variant, cached):
     assert p["residual_out_cached"] == cached
 
 
+# More than 8 ranks: the automatic choice takes the scalar kernel for rows of at most 4096
+# elements from 4 rows per CU (8 at W=16); fewer rows, longer rows, at most 8 ranks or a
+# tuned lane layout keep their plans.
+@pytest.mark.parametrize("W,T,H,variant", [
+    (12, 1024, 4096, A.ARRMS_VARIANT_SCALAR), (12, 1023, 4096, A.ARRMS_VARIANT_ROW),
+    (9, 1024, 2048, A.ARRMS_VARIANT_SCALAR), (15, 4096, 2048, A.ARRMS_VARIANT_SCALAR),
+    (16, 2048, 2048, A.ARRMS_VARIANT_SCALAR), (16, 2047, 2048, A.ARRMS_VARIANT_ROW),
+    (16, 4096, 4104, A.ARRMS_VARIANT_SPLITH), (8, 16384, 2048, A.ARRMS_VARIANT_ROW),
+    (12, 4096, 8192, A.ARRMS_VARIANT_SPLITH), (10, 1024, 2560, A.ARRMS_VARIANT_SCALAR),
+])
+def test_many_ranks_take_the_scalar_kernel(W, T, H, variant):
+    rc, p = plan(W, T, H)
+    assert rc == A.ARRMS_OK and p["variant"] == variant, (W, T, H, p)
+    if variant == A.ARRMS_VARIANT_SCALAR:
+        assert p["elems_per_load"] == (4 if H % 4 == 0 else 2)
+
+
+def test_many_ranks_rule_scales_with_cus_and_respects_tuning():
+    lim = dict(LIM)
+    rc, p = plan(12, 512, 2048, cu=128, lim=lim)                # 4 rows per CU on 128 CUs
+    assert p["variant"] == A.ARRMS_VARIANT_SCALAR
+    rc, p = plan(12, 511, 2048, cu=128, lim=lim)
+    assert p["variant"] == A.ARRMS_VARIANT_ROW
+    for t in (dict(vec_per_thread=1), dict(threads_per_row=256), dict(rows_per_block=1)):
+        rc, p = plan(12, 4096, 2048, tuning=A.arrms_tuning_t.make(**t))
+        assert rc == A.ARRMS_OK and p["variant"] == A.ARRMS_VARIANT_ROW, t
+
+
 def test_scalar_lanes_tuning():
     """threads_per_row sets the scalar kernel's lanes per row when it is a multiple of 64."""
     for tpr, want in ((256, 256), (512, 512), (64, 64), (1024, 1024), (32, 640)):

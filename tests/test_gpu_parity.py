@@ -129,6 +129,13 @@ def test_residual_out_store_policies(W, T, H, variant, store):
     assert plan["residual_out_cached"] == store - 1
 
 
+# More than 8 ranks with enough rows: the automatic plan is the scalar kernel's rank loop.
+@pytest.mark.parametrize("W,T,H", [(12, 1024, 4096), (16, 2048, 2048), (9, 1030, 1000), (11, 1024, 2046)])
+def test_many_ranks_scalar_plan(W, T, H):
+    plan, _ = parity(W, T, H, seed=W * 1000 + H)
+    assert plan["variant"] == SCALAR
+
+
 def _shifted(t, off, dev):
     """A copy of CPU tensor t on the GPU, starting `off` bytes past a 256-byte boundary."""
     buf = torch.zeros(t.numel() + 16, dtype=torch.bfloat16, device=dev)
