@@ -51,7 +51,7 @@ EXPORTS = ("arrms_create", "arrms_fused", "arrms_destroy", "arrms_status_string"
 class arrms_plan_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("variant", "grid", "block", "vec_per_thread", "threads_per_row",
                                             "rows_per_block", "chunks_per_row", "kernels", "blocks", "xcd_chunk",
-                                            "elems_per_load", "residual_out_cached")]
+                                            "elems_per_load", "residual_out_cached", "rank_loop")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -84,6 +84,62 @@ __global__ void __launch_bounds__(kReduceLanes) reduce_kernel(const ReduceArgs<(
     }
 }
 
+// The same sum for more than 8 ranks with the ranks added one load round at a time:
+// x_0's groups, then each further rank's groups added in rank order (the arithmetic is
+// unchanged).  Only L groups of one rank are in registers at a time, so a CU runs many
+// workgroups, which pays once each CU has enough of them to cover the round trips.
+template <int L, int E>
+__global__ void __launch_bounds__(kReduceLanes) reduce_loop_kernel(const ReduceArgs<kMaxWorld> a) {
+    typedef typename Group<E>::T G;
+    typedef Buf<E> B;
+    const int block = logical_block(a.xcd_chunk, a.blocks);
+    if (block < 0) return;
+    const long long ng = a.count / E;
+    const long long g0 = static_cast<long long>(block) * kReduceLanes * L;
+    if (g0 < ng) {
+        const long long span = ng - g0 < kReduceLanes * L ? ng - g0 : kReduceLanes * L;
+        const int bytes = static_cast<int>(span) * static_cast<int>(sizeof(G));
+        const size_t first = static_cast<size_t>(g0) * E;
+        int off[L];
+#pragma unroll
+        for (int k = 0; k < L; ++k) off[k] = (k * kReduceLanes + static_cast<int>(threadIdx.x)) * static_cast<int>(sizeof(G));
+        float acc[L][E];
+        {
+            const Rsrc r0 = make_rsrc(static_cast<const uint16_t*>(a.x.p[0]) + first, bytes);
+            G v[L];
+#pragma unroll
+            for (int k = 0; k < L; ++k) v[k] = B::template ld<kBufNT>(r0, off[k]);
+#pragma unroll
+            for (int k = 0; k < L; ++k)
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[k][e] = Group<E>::get(v[k], e);
+        }
+        for (int r = 1; r < a.world; ++r) {
+            const Rsrc rr = make_rsrc(static_cast<const uint16_t*>(a.x.p[r]) + first, bytes);
+            G v[L];
+#pragma unroll
+            for (int k = 0; k < L; ++k) v[k] = B::template ld<kBufNT>(rr, off[k]);
+#pragma unroll
+            for (int k = 0; k < L; ++k)
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[k][e] = acc[k][e] + Group<E>::get(v[k], e);
+        }
+        const Rsrc rout = make_rsrc(static_cast<uint16_t*>(a.reduced) + first, bytes);
+#pragma unroll
+        for (int k = 0; k < L; ++k) B::template st<kBufNT>(pack<E>(acc[k]), rout, off[k]);
+    }
+    if (block == a.blocks - 1) {  // the head and the tail, element-wise
+        const long long tail0 = ng * E;
+        const int extra = a.head + static_cast<int>(a.count - tail0);
+        for (int j = threadIdx.x; j < extra; j += kReduceLanes) {
+            const long long e = j < a.head ? static_cast<long long>(j - a.head) : tail0 + (j - a.head);
+            float acc = lo_f32(static_cast<const uint16_t*>(a.x.p[0])[e]);
+            for (int r = 1; r < a.world; ++r) acc = acc + lo_f32(static_cast<const uint16_t*>(a.x.p[r])[e]);
+            static_cast<uint16_t*>(a.reduced)[e] = cvt1(acc);
+        }
+    }
+}
+
 template <int L, int E>
 const void* reduce_fn(int world) {
     switch (world) {
@@ -119,6 +175,17 @@ hipError_t launch_reduce_with(const void* fn, const Args& a, int grid, hipStream
 
 hipError_t launch_reduce(const Args& a, int vpt, int grid, int block, hipStream_t s) {
     const void* fn = nullptr;
+    if (a.rank_loop && a.world > 8) {
+        switch (a.elems_per_load) {
+            case 8: fn = reinterpret_cast<const void*>(&reduce_loop_kernel<1, 8>); break;
+            case 4: fn = reinterpret_cast<const void*>(&reduce_loop_kernel<2, 4>); break;
+            case 2: fn = reinterpret_cast<const void*>(&reduce_loop_kernel<4, 2>); break;
+            case 1: fn = reinterpret_cast<const void*>(&reduce_loop_kernel<8, 1>); break;
+            default: return hipErrorInvalidValue;
+        }
+        if (vpt > 1 || block != kReduceLanes || a.head < 0 || a.head >= a.elems_per_load) return hipErrorInvalidValue;
+        return launch_reduce_with<kMaxWorld>(fn, a, grid, s);
+    }
     switch (a.elems_per_load) {
         case 8:
             switch (vpt) {

@@ -97,6 +97,7 @@ int main(int argc, char** argv) {
             int want = tp && tp->residual_out_store == 2;
             if (p.variant == ARRMS_VARIANT_SPLITH) want = 1;
             if (p.residual_out_cached != want) return fail("residual_out store policy", i);
+            if (p.rank_loop != (p.variant == ARRMS_VARIANT_SCALAR && W > 8)) return fail("fused rank loop", i);
         }
         if (rc == ARRMS_OK && tp && (tp->residual_out_store < 0 || tp->residual_out_store > 2 || tp->scalar_elems == 3))
             return fail("invalid tuning accepted", i);
@@ -125,6 +126,7 @@ int main(int argc, char** argv) {
             if ((p.variant == ARRMS_VARIANT_REDUCE) != (e == 8)) return fail("reduce variant", i);
             if (p.variant != ARRMS_VARIANT_REDUCE && p.variant != ARRMS_VARIANT_REDUCE_SCALAR)
                 return fail("reduce variant kind", i);
+            if (p.rank_loop != (W > 8 && (long long)p.blocks >= 8LL * cu)) return fail("reduce rank loop", i);
             // every pointer has the same offset modulo 2E bytes, and the groups cover the elements
             int e2 = 0, head = -1;
             arrms::reduce_alignment(parts, W, no, count, e, &e2, &head);

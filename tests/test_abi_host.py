@@ -440,6 +440,22 @@ def test_many_ranks_rule_scales_with_cus_and_respects_tuning():
         assert rc == A.ARRMS_OK and p["variant"] == A.ARRMS_VARIANT_ROW, t
 
 
+@pytest.mark.parametrize("W,T,loop", [(12, 2048, 1), (12, 2047, 0), (16, 4096, 1), (9, 2048, 1), (8, 16384, 0),
+                                       (16, 1024, 0), (16, 256, 0)])
+def test_reduce_rank_loop(W, T, loop):
+    """More than 8 ranks: the rank sum adds them one load round at a time from 8
+    workgroups per CU (2048 elements per workgroup: T*H >= 8 * 256 * 2048)."""
+    rc, p = rplan(W, T, 2048)
+    assert rc == A.ARRMS_OK and p["rank_loop"] == loop, p
+    assert p["blocks"] == T * 2048 // 2048
+
+
+def test_scalar_rank_loop_flag():
+    assert plan(12, 64, 2047)[1]["rank_loop"] == 1 and plan(8, 64, 2047)[1]["rank_loop"] == 0
+    assert plan(16, 4096, 2048)[1]["rank_loop"] == 1                     # the many-ranks scalar plan
+    assert plan(16, 33, 2048)[1]["rank_loop"] == 0                       # row kernel
+
+
 def test_scalar_lanes_tuning():
     """threads_per_row sets the scalar kernel's lanes per row when it is a multiple of 64."""
     for tpr, want in ((256, 256), (512, 512), (64, 64), (1024, 1024), (32, 640)):

@@ -32,7 +32,10 @@ def _metadata(src, tmp_path):
 
 
 def _world(name):
-    """Template W of a kernel name (None for kernels without one)."""
+    """Template W of a kernel name (None for kernels without one; 0 for the rank-loop
+    rank sum, which serves 9-16 ranks like the generic instances)."""
+    if "reduce_loop_kernel" in name:
+        return 0
     m = re.search(r"(row_kernel|splith_partial_kernel|scalar_kernel|reduce_kernel)ILi(\d+)E", name)
     return int(m.group(2)) if m else None
 
