@@ -85,8 +85,8 @@ typedef struct {
     int residual_out_cached; /* 1: residual_out written with write-back stores, 0: with streaming (non-temporal)
                                 stores; split-H always 1 (its second kernel reads residual_out back); rank sum 0 */
     int rank_loop;       /* 1: the ranks after x_0 are added one load round at a time (the scalar kernel with more
-                            than 8 ranks; the rank sum with more than 8 ranks and at least 8 workgroups per CU);
-                            0: every rank's loads are issued together */
+                            than 8 ranks, or chosen automatically for 6-8 ranks; the rank sum with more than 8 ranks
+                            and at least 8 workgroups per CU); 0: every rank's loads are issued together */
 } arrms_plan_t;
 
 /* Optional tuning overrides; 0 (or -1 where stated) keeps the automatic choice.
@@ -94,7 +94,7 @@ typedef struct {
 typedef struct {
     int vec_per_thread;    /* row / split-H: 1, 2, 4 or 8 */
     int threads_per_row;   /* row: 16, 32 or a multiple of 64 up to 1024; scalar: lanes per row when a multiple
-                              of 64 (capped at 1024, or 512 for more than 8 ranks) */
+                              of 64 (capped at 1024) */
     int splith_block;      /* split-H: threads per workgroup, 64..1024, multiple of 64 */
     int splith_max_tokens; /* automatic variant uses split-H when tokens <= this; -1 automatic */
     int xcd_chunk;         /* -1 automatic; 0 hardware round-robin; K > 0 runs of K blocks per XCD */

@@ -242,14 +242,17 @@ int plan_splith(int cu_count, int max_hidden, int world, int tokens, int hidden,
 }
 
 // Scalar plan: one row per workgroup, 8 elements per lane per span: enough whole
-// waves to cover the row in one span, at most 1024 lanes (512 for more than 8
-// ranks: the kernels' __launch_bounds__); a longer row runs on 256 lanes.  Loads are `elems` BF16
+// waves to cover the row in one span, at most 1024 lanes (the kernels'
+// __launch_bounds__); a longer row runs on 256 lanes.  More than 8 ranks, or
+// rank_loop, take the generic instance, which adds the ranks after x_0 one load
+// round at a time.  Loads are `elems` BF16
 // elements wide (the widest that H and every pointer's alignment allow, at most
 // the tuned width).  XCD runs as in the row variant (about 3 MiB of traffic per run).
 // The kernel aligns its lanes to 128-byte lines by rotating a one-span row, so a
 // row takes no lanes beyond its own length.
-void plan_scalar(int world, int tokens, int hidden, int elems, const arrms_tuning_t* t, arrms_plan_t* p) {
-    const int max_block = world > 8 ? 512 : 1024;
+void plan_scalar(int world, int tokens, int hidden, int elems, const arrms_tuning_t* t, arrms_plan_t* p,
+                 bool rank_loop = false) {
+    const int max_block = 1024;
     int block = ((hidden + 7) / 8 + 63) / 64 * 64;
     // A row longer than one span of the largest workgroup takes several spans anyway;
     // 4-wave workgroups run them 9-13 % faster than the largest ones (measured on
@@ -268,7 +271,7 @@ void plan_scalar(int world, int tokens, int hidden, int elems, const arrms_tunin
     p->kernels = 1;
     p->elems_per_load = elems;
     p->residual_out_cached = residual_out_cached(t);
-    p->rank_loop = world > 8;  // the generic instance adds ranks 1.. one at a time
+    p->rank_loop = world > 8 || rank_loop;  // the generic instance adds ranks 1.. one at a time
     int k = 0;
     if (p->blocks >= 64) {
         const long row_bytes = 2L * (world + 3) * hidden;
@@ -279,21 +282,35 @@ void plan_scalar(int world, int tokens, int hidden, int elems, const arrms_tunin
 }
 
 // More than 8 ranks: the automatic choice takes the scalar kernel for rows of one
-// span (H <= 4096 on its 512 lanes) once there are enough rows to overlap its rank
+// span (H <= 8192 on its 1024 lanes) once there are enough rows to overlap its rank
 // loop.  That kernel keeps only x_0, the residual and the weight in registers and adds
 // the other ranks one load round at a time, so it runs many more workgroups per CU
 // than the row kernel holding all 9-16 ranks; per row it pays one memory round trip
 // per rank.  Measured on MI355X (4.5 GB rotation) against the row kernel: 8-30 %
 // faster from T = 1024 at W = 9, 10, 12 and H = 2048-4096 (the generic 9-15-rank row
 // kernel), and 7-10 % faster from T = 2048 at W = 16 (its own row instance), but
-// 8 % slower at W = 16 T = 1024 and 1.3-2.3x slower at T <= 512.  Rows over 4096
-// elements (split-H or several scalar spans) measured even, so they keep their plan;
-// a tuned lane layout keeps the row kernel.
+// 8 % slower at W = 16 T = 1024 and 1.3-2.3x slower at T <= 512.  Rows of 4104-8192
+// elements, which would otherwise take split-H, gain 13-38 % (W = 12, 16 at H = 6144,
+// 8192); longer rows, on several spans, measured even, so they keep their plan; a
+// tuned lane layout keeps the row kernel.
 bool many_ranks_scalar(int cu_count, int world, int tokens, int hidden, const arrms_tuning_t* t) {
-    if (world <= 8 || hidden > 8 * 512) return false;
+    if (world <= 8 || hidden > 8 * 1024) return false;
     if (t && (t->vec_per_thread || t->threads_per_row || t->rows_per_block)) return false;
     const long long min_rows = static_cast<long long>(world == 16 ? 8 : 4) * cu_count;
     return tokens >= min_rows;
+}
+
+// Six to eight ranks: the rank loop also beats the row kernel, by 2-6 % (W = 6, 7, 8 at
+// H = 2048, 4096, 8192, T >= 2048, measured on MI355X), but only on workgroups of 256,
+// 512 or 1024 lanes: those divide a CU's 32 wave slots, which the rank loop needs full
+// to cover its round trips.  With 384-896 lanes it lost 1-7 %, and below 8 rows per CU
+// 10 % (W=8 H=2048 T=1024).  W <= 5 measured even or slower.
+bool mid_ranks_rank_loop(int cu_count, int world, int tokens, int hidden, const arrms_tuning_t* t) {
+    if (world < 6 || world > 8) return false;
+    if (t && (t->vec_per_thread || t->threads_per_row || t->rows_per_block || t->scalar_elems)) return false;
+    const int lanes = ((hidden + 7) / 8 + 63) / 64 * 64;
+    if (lanes != 256 && lanes != 512 && lanes != 1024) return false;
+    return tokens >= 8LL * cu_count;
 }
 
 // Widest load, in BF16 elements, that H and the OR of all pointer addresses allow.
@@ -415,6 +432,11 @@ int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
         plan_scalar(world, tokens, hidden, elems, tuning, plan);
         return ARRMS_OK;
     }
+    // Six to eight ranks on power-of-two workgroups, enough rows: its rank loop.
+    if (tokens > split_max && mid_ranks_rank_loop(cu_count, world, tokens, hidden, tuning)) {
+        plan_scalar(world, tokens, hidden, elems, tuning, plan, true);
+        return ARRMS_OK;
+    }
     // The automatic choice always finds a plan: tuning overrides that no vector
     // kernel can honour end in the scalar kernel (same results).
     if (hidden > ARRMS_ROW_MAX_HIDDEN || tokens <= split_max) {
@@ -532,6 +554,7 @@ hipError_t launch_fused(const arrms_plan_t& p, const void* const* partials, int 
     a.xcd_chunk = p.xcd_chunk;
     a.elems_per_load = p.elems_per_load;
     a.ro_cached = p.residual_out_cached;
+    a.rank_loop = p.rank_loop;
     switch (p.variant) {
         case ARRMS_VARIANT_ROW: return launch_row(a, p.vec_per_thread, p.grid, p.block, stream);
         case ARRMS_VARIANT_SPLITH: return launch_splith(a, p.vec_per_thread, p.grid, p.block, stream);

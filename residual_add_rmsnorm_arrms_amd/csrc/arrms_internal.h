@@ -43,7 +43,7 @@ struct Args {
     int elems_per_load;     // scalar: BF16 elements per load (1, 2 or 4); rank sum: 1, 2, 4 or 8
     int head;               // rank sum only: elements before the aligned start of x.p[] / reduced
     int ro_cached;          // row, scalar: 1 write-back stores for residual_out, 0 streaming stores
-    int rank_loop;          // rank sum with more than 8 ranks: 1 add the ranks one load round at a time
+    int rank_loop;          // rank sum, scalar: 1 add the ranks after x_0 one load round at a time
     long long count;        // rank sum only: elements from the aligned start (tokens * hidden - head)
 };
 

@@ -238,11 +238,11 @@ __global__ void __launch_bounds__(1024) splith_norm_kernel(const SplitNormArgs a
 // a lane's first group of the first span can wrap or fall before the row.
 constexpr int kScalarSpan = 8;
 
-// Largest workgroup of a scalar kernel: the generic-W instances keep up to 16 ranks'
-// loads in registers and get the larger register budget of 512-lane workgroups.  The
-// host planner uses the same limits.
+// Largest workgroup of a scalar kernel (the host planner uses the same limit).  The
+// generic-W instance holds only x_0's loads (its rank loop adds the others one round
+// at a time), so it fits 1024 lanes as the specialised ones do.
 template <int W>
-constexpr int scalar_max_threads() { return W == 0 ? 512 : 1024; }
+constexpr int scalar_max_threads() { return 1024; }
 
 template <int W, int E, bool RC>
 __global__ void __launch_bounds__(scalar_max_threads<W>()) scalar_kernel(const ScalarArgs<(W > 0 ? W : kMaxWorld)> a) {
@@ -426,7 +426,7 @@ hipError_t launch_splith_partial_with(const void* fn, const Args& a, int grid, i
 template <int WA>
 hipError_t launch_scalar_with(const void* fn, const Args& a, int grid, int block, hipStream_t s) {
     const int e_code = a.elems_per_load == 4 ? 2 : (a.elems_per_load == 2 ? 1 : 0);
-    if (block % 64 || block < 64 || block > (WA > 8 ? 512 : 1024) || a.world > 31 || a.hidden < 1 ||
+    if (block % 64 || block < 64 || block > 1024 || a.world > 31 || a.hidden < 1 ||
         a.hidden > 0x1ffff ||
         (1 << e_code) != a.elems_per_load || a.hidden % a.elems_per_load)
         return hipErrorInvalidValue;
@@ -571,12 +571,15 @@ const void* scalar_fn(int world) {
 hipError_t launch_scalar(const Args& a, int grid, int block, hipStream_t s) {
     const void* fn = nullptr;
     const bool rc = a.ro_cached != 0;
+    // the rank loop is the generic instance (any rank count, ranks after x_0 added one at a time)
+    const int w = a.rank_loop ? 0 : a.world;
     switch (a.elems_per_load) {
-        case 1: fn = rc ? scalar_fn<1, true>(a.world) : scalar_fn<1, false>(a.world); break;
-        case 2: fn = rc ? scalar_fn<2, true>(a.world) : scalar_fn<2, false>(a.world); break;
-        case 4: fn = rc ? scalar_fn<4, true>(a.world) : scalar_fn<4, false>(a.world); break;
+        case 1: fn = rc ? scalar_fn<1, true>(w) : scalar_fn<1, false>(w); break;
+        case 2: fn = rc ? scalar_fn<2, true>(w) : scalar_fn<2, false>(w); break;
+        case 4: fn = rc ? scalar_fn<4, true>(w) : scalar_fn<4, false>(w); break;
         default: return hipErrorInvalidValue;
     }
+    if (a.rank_loop) return launch_scalar_with<kMaxWorld>(fn, a, grid, block, s);
     switch (a.world) {
         case 1: return launch_scalar_with<1>(fn, a, grid, block, s);
         case 2: return launch_scalar_with<2>(fn, a, grid, block, s);

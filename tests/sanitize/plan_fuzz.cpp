@@ -87,7 +87,7 @@ int main(int argc, char** argv) {
                 if (!tuned_block && (long)p.block * 8 < H && p.block != 256) return fail("scalar span", i);
                 if (!tuned_block && (long)p.block * 8 >= H && (long)(p.block - 64) * 8 >= H)
                     return fail("scalar lanes", i);
-                if (p.block > (W > 8 ? 512 : 1024)) return fail("scalar block", i);
+                if (p.block > 1024) return fail("scalar block", i);
             } else {
                 return fail("variant", i);
             }
@@ -97,7 +97,13 @@ int main(int argc, char** argv) {
             int want = tp && tp->residual_out_store == 2;
             if (p.variant == ARRMS_VARIANT_SPLITH) want = 1;
             if (p.residual_out_cached != want) return fail("residual_out store policy", i);
-            if (p.rank_loop != (p.variant == ARRMS_VARIANT_SCALAR && W > 8)) return fail("fused rank loop", i);
+            // the rank loop: always for the scalar kernel beyond 8 ranks; for 6-8 ranks only on
+            // power-of-two workgroups with at least 8 rows per CU; never for the other variants
+            if (p.variant == ARRMS_VARIANT_SCALAR && W > 8 && !p.rank_loop) return fail("fused rank loop", i);
+            if (p.rank_loop && (p.variant != ARRMS_VARIANT_SCALAR ||
+                                (W <= 8 && (W < 6 || (long long)T < 8LL * cu ||
+                                            (p.block != 256 && p.block != 512 && p.block != 1024)))))
+                return fail("fused rank loop shape", i);
         }
         if (rc == ARRMS_OK && tp && (tp->residual_out_store < 0 || tp->residual_out_store > 2 || tp->scalar_elems == 3))
             return fail("invalid tuning accepted", i);

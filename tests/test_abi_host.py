@@ -281,7 +281,7 @@ def test_create_rejects_bad_limits():
 
 @pytest.mark.parametrize("W,T,H,variant,vpt,tpr,k", [
     (4, 4096, 2048, A.ARRMS_VARIANT_ROW, 1, 256, 64),      # prefill: 256-lane rows, 64-row XCD runs
-    (8, 8192, 8192, A.ARRMS_VARIANT_ROW, 2, 512, 16),
+    (8, 8192, 8192, A.ARRMS_VARIANT_SCALAR, 0, 1024, 16),  # large_hidden: the rank loop on 1024 lanes
     (8, 16383, 5120, A.ARRMS_VARIANT_ROW, 2, 512, 16),     # 8-wave rows beat exact 5-wave rows
     (4, 16, 2048, A.ARRMS_VARIANT_ROW, 1, 256, 0),         # decode, small rows: one kernel
     (8, 1, 8192, A.ARRMS_VARIANT_SPLITH, 1, 64, 0),        # decode, large rows: split over CUs
@@ -412,21 +412,40 @@ def test_residual_out_store_policy(W, T, H, variant, cached):
     assert p["residual_out_cached"] == cached
 
 
-# More than 8 ranks: the automatic choice takes the scalar kernel for rows of at most 4096
-# elements from 4 rows per CU (8 at W=16); fewer rows, longer rows, at most 8 ranks or a
+# More than 8 ranks: the automatic choice takes the scalar kernel for rows of at most 8192
+# elements from 4 rows per CU (8 at W=16); fewer rows, longer rows, at most 5 ranks or a
 # tuned lane layout keep their plans.
 @pytest.mark.parametrize("W,T,H,variant", [
     (12, 1024, 4096, A.ARRMS_VARIANT_SCALAR), (12, 1023, 4096, A.ARRMS_VARIANT_ROW),
     (9, 1024, 2048, A.ARRMS_VARIANT_SCALAR), (15, 4096, 2048, A.ARRMS_VARIANT_SCALAR),
     (16, 2048, 2048, A.ARRMS_VARIANT_SCALAR), (16, 2047, 2048, A.ARRMS_VARIANT_ROW),
-    (16, 4096, 4104, A.ARRMS_VARIANT_SPLITH), (8, 16384, 2048, A.ARRMS_VARIANT_ROW),
-    (12, 4096, 8192, A.ARRMS_VARIANT_SPLITH), (10, 1024, 2560, A.ARRMS_VARIANT_SCALAR),
+    (16, 4096, 4104, A.ARRMS_VARIANT_SCALAR), (5, 16384, 2048, A.ARRMS_VARIANT_ROW),
+    (12, 4096, 8192, A.ARRMS_VARIANT_SCALAR), (12, 4096, 8200, A.ARRMS_VARIANT_SPLITH),
+    (10, 1024, 2560, A.ARRMS_VARIANT_SCALAR),
 ])
 def test_many_ranks_take_the_scalar_kernel(W, T, H, variant):
     rc, p = plan(W, T, H)
     assert rc == A.ARRMS_OK and p["variant"] == variant, (W, T, H, p)
     if variant == A.ARRMS_VARIANT_SCALAR:
         assert p["elems_per_load"] == (4 if H % 4 == 0 else 2)
+
+
+# Six to eight ranks: the scalar kernel's rank loop on power-of-two workgroups (H rounding
+# up to 256, 512 or 1024 lanes) from 8 rows per CU; other lane counts keep the row kernel.
+@pytest.mark.parametrize("W,T,H,loop", [
+    (8, 8192, 8192, True), (8, 2048, 2048, True), (8, 2047, 2048, False), (6, 4096, 4096, True),
+    (7, 4096, 8192, True), (8, 16383, 5120, False), (8, 4096, 3072, False), (5, 4096, 8192, False),
+    (8, 4096, 2040, True), (8, 4096, 7168, False),
+])
+def test_mid_ranks_rank_loop(W, T, H, loop):
+    rc, p = plan(W, T, H)
+    assert rc == A.ARRMS_OK
+    if loop:
+        assert p["variant"] == A.ARRMS_VARIANT_SCALAR and p["rank_loop"] == 1 and p["block"] in (256, 512, 1024), p
+    else:
+        assert p["variant"] == A.ARRMS_VARIANT_ROW and p["rank_loop"] == 0, p
+    t = A.arrms_tuning_t.make(vec_per_thread=1 if H <= 4096 else 2)   # a tuned layout keeps the row kernel
+    assert plan(W, T, H, tuning=t)[1]["variant"] == A.ARRMS_VARIANT_ROW
 
 
 def test_many_ranks_rule_scales_with_cus_and_respects_tuning():
@@ -454,6 +473,7 @@ def test_scalar_rank_loop_flag():
     assert plan(12, 64, 2047)[1]["rank_loop"] == 1 and plan(8, 64, 2047)[1]["rank_loop"] == 0
     assert plan(16, 4096, 2048)[1]["rank_loop"] == 1                     # the many-ranks scalar plan
     assert plan(16, 33, 2048)[1]["rank_loop"] == 0                       # row kernel
+    assert plan(8, 4096, 2047)[1]["rank_loop"] == 0                      # odd rows: the specialised instance
 
 
 def test_scalar_lanes_tuning():
@@ -461,8 +481,8 @@ def test_scalar_lanes_tuning():
     for tpr, want in ((256, 256), (512, 512), (64, 64), (1024, 1024), (32, 640)):
         rc, p = plan(8, 100, 5119, tuning=A.arrms_tuning_t.make(threads_per_row=tpr))
         assert rc == A.ARRMS_OK and p["variant"] == A.ARRMS_VARIANT_SCALAR and p["block"] == want, (tpr, p)
-    rc, p = plan(12, 100, 5119, tuning=A.arrms_tuning_t.make(threads_per_row=1024))   # > 8 ranks: at most 512
-    assert p["block"] == 512
+    rc, p = plan(12, 100, 5119, tuning=A.arrms_tuning_t.make(threads_per_row=1024))   # any rank count: up to 1024
+    assert p["block"] == 1024
 
 
 def test_residual_out_store_tuning():

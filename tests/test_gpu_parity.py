@@ -87,7 +87,7 @@ def test_world_sweep(W, variant):
 
 
 # The scalar variant walks a row in spans of 8 * lanes elements: a row that fits one
-# span of at most 1024 lanes (512 beyond 8 ranks) gets just enough lanes and keeps
+# span of at most 1024 lanes gets just enough lanes and keeps
 # residual_out in registers; a longer row runs on 256 lanes over several spans and
 # re-reads it.  Single-element rows,
 # rows ending one element into a new span, in place, generic W and the largest H.
@@ -100,7 +100,7 @@ def test_scalar_spans(W, T, H, inplace):
     plan, _ = parity(W, T, H, variant=SCALAR, inplace=inplace, seed=H)
     assert plan["variant"] == SCALAR
     one_span = -(-(-(-H // 8)) // 64) * 64
-    assert plan["block"] == (one_span if one_span <= (512 if W > 8 else 1024) else 256)
+    assert plan["block"] == (one_span if one_span <= 1024 else 256)
 
 
 # The scalar variant loads 4, 2 or 1 BF16 elements at a time: the widest that H and
@@ -129,8 +129,11 @@ def test_residual_out_store_policies(W, T, H, variant, store):
     assert plan["residual_out_cached"] == store - 1
 
 
-# More than 8 ranks with enough rows: the automatic plan is the scalar kernel's rank loop.
-@pytest.mark.parametrize("W,T,H", [(12, 1024, 4096), (16, 2048, 2048), (9, 1030, 1000), (11, 1024, 2046)])
+# More than 8 ranks with enough rows, or 6-8 ranks on power-of-two workgroups: the automatic
+# plan is the scalar kernel's rank loop.
+@pytest.mark.parametrize("W,T,H", [(12, 1024, 4096), (16, 2048, 2048), (9, 1030, 1000), (11, 1024, 2046),
+                                   (12, 1024, 8192), (10, 1100, 6000), (8, 2048, 2048), (6, 2100, 4096),
+                                   (7, 2048, 8184)])
 def test_many_ranks_scalar_plan(W, T, H):
     plan, _ = parity(W, T, H, seed=W * 1000 + H)
     assert plan["variant"] == SCALAR
