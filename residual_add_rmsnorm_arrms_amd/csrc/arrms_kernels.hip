@@ -204,10 +204,11 @@ __global__ void __launch_bounds__(1024) splith_norm_kernel(const SplitNormArgs a
 
 // -------------------------------------------------------------- scalar variant
 // Rows that the 16-byte kernels cannot take (H % 8 != 0, or a pointer not 16-byte
-// aligned).  Loads are E BF16 elements wide (E = 4, 2 or 1: 8-, 4- or 2-byte
-// loads), the widest that H and the alignment of every pointer allow.  One row per
-// workgroup of n lanes (n <= 1024, or 512 for more than 8 ranks), XCD runs as in
-// the row variant.  The row is walked in spans of kScalarSpan * n elements; in a
+// aligned), and, through the generic instance's rank loop (W = 0: only x_0 loaded
+// up front, the other ranks added one load round at a time), calls with many ranks
+// that the planner gives it.  Loads are E BF16 elements wide (E = 4, 2 or 1: 8-, 4-
+// or 2-byte loads), the widest that H and the alignment of every pointer allow.  One
+// row per workgroup of n lanes (n <= 1024), XCD runs as in the row variant.  The row is walked in spans of kScalarSpan * n elements; in a
 // span lane l owns the E-element groups l, l + n, ..., l + (8 / E - 1) * n, so each
 // load instruction of a wave covers 128 * E contiguous bytes and a lane moves 16
 // bytes per input per span, as in the row variant.
