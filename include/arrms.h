@@ -85,7 +85,7 @@ typedef struct {
     int residual_out_cached; /* 1: residual_out written with write-back stores, 0: with streaming (non-temporal)
                                 stores; split-H always 1 (its second kernel reads residual_out back); rank sum 0 */
     int rank_loop;       /* 1: the ranks after x_0 are added one load round at a time (the scalar kernel with more
-                            than 8 ranks, or chosen automatically for 6-8 ranks; the rank sum with more than 8 ranks
+                            than 8 ranks, or chosen automatically for 6-8 ranks; the rank sum with 6 ranks or more
                             and at least 8 workgroups per CU); 0: every rank's loads are issued together */
 } arrms_plan_t;
 

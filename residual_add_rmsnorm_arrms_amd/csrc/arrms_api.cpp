@@ -509,12 +509,12 @@ int plan_reduce(int cu_count, const arrms_tuning_t* tuning, int max_world, int m
     plan->vec_per_thread = elems == 8 ? vpt : 0;
     plan->elems_per_load = elems;
     plan->blocks = static_cast<int>(blocks);
-    // More than 8 ranks: add them one load round at a time once every CU has at least 8
-    // workgroups (measured on MI355X, W = 9-16, T*H = 0.5-32 M elements: 4-11 % faster
-    // from 16 workgroups per CU, 80.9 % of HBM peak at W=16 T=4096 H=2048; 10 % slower at
-    // 4 per CU and 1.8x at 1 per CU, where the workgroups cannot cover the rank loop's
-    // round trips).
-    plan->rank_loop = world > 8 && blocks >= 8LL * cu_count;
+    // Six ranks or more: add them one load round at a time once every CU has at least 8
+    // workgroups (measured on MI355X, 4.5 GB rotation: W = 9-16 4-11 % faster from 8
+    // workgroups per CU, 80.9 % of HBM peak at W=16 T=4096 H=2048; W = 6 and 8 3-5 %
+    // faster; W = 5 even, W = 4 up to 5 % slower; at 4 workgroups per CU 10 % slower and
+    // at 1 per CU 1.8x, where the workgroups cannot cover the loop's round trips).
+    plan->rank_loop = world >= 6 && blocks >= 8LL * cu_count;
     int k = 0;
     if (plan->blocks >= 64) {
         const long block_bytes = 2L * elems * per_block * (world + 1);

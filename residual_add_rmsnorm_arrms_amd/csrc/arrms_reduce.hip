@@ -84,7 +84,7 @@ __global__ void __launch_bounds__(kReduceLanes) reduce_kernel(const ReduceArgs<(
     }
 }
 
-// The same sum for more than 8 ranks with the ranks added one load round at a time:
+// The same sum for six ranks or more with the ranks added one load round at a time:
 // x_0's groups, then each further rank's groups added in rank order (the arithmetic is
 // unchanged).  Only L groups of one rank are in registers at a time, so a CU runs many
 // workgroups, which pays once each CU has enough of them to cover the round trips.
@@ -175,7 +175,7 @@ hipError_t launch_reduce_with(const void* fn, const Args& a, int grid, hipStream
 
 hipError_t launch_reduce(const Args& a, int vpt, int grid, int block, hipStream_t s) {
     const void* fn = nullptr;
-    if (a.rank_loop && a.world > 8) {
+    if (a.rank_loop) {
         switch (a.elems_per_load) {
             case 8: fn = reinterpret_cast<const void*>(&reduce_loop_kernel<1, 8>); break;
             case 4: fn = reinterpret_cast<const void*>(&reduce_loop_kernel<2, 4>); break;

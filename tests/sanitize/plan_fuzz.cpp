@@ -132,7 +132,7 @@ int main(int argc, char** argv) {
             if ((p.variant == ARRMS_VARIANT_REDUCE) != (e == 8)) return fail("reduce variant", i);
             if (p.variant != ARRMS_VARIANT_REDUCE && p.variant != ARRMS_VARIANT_REDUCE_SCALAR)
                 return fail("reduce variant kind", i);
-            if (p.rank_loop != (W > 8 && (long long)p.blocks >= 8LL * cu)) return fail("reduce rank loop", i);
+            if (p.rank_loop != (W >= 6 && (long long)p.blocks >= 8LL * cu)) return fail("reduce rank loop", i);
             // every pointer has the same offset modulo 2E bytes, and the groups cover the elements
             int e2 = 0, head = -1;
             arrms::reduce_alignment(parts, W, no, count, e, &e2, &head);

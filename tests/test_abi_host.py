@@ -459,10 +459,10 @@ def test_many_ranks_rule_scales_with_cus_and_respects_tuning():
         assert rc == A.ARRMS_OK and p["variant"] == A.ARRMS_VARIANT_ROW, t
 
 
-@pytest.mark.parametrize("W,T,loop", [(12, 2048, 1), (12, 2047, 0), (16, 4096, 1), (9, 2048, 1), (8, 16384, 0),
-                                       (16, 1024, 0), (16, 256, 0)])
+@pytest.mark.parametrize("W,T,loop", [(12, 2048, 1), (12, 2047, 0), (16, 4096, 1), (9, 2048, 1), (8, 16384, 1),
+                                       (6, 2048, 1), (5, 16384, 0), (4, 16384, 0), (16, 1024, 0), (16, 256, 0)])
 def test_reduce_rank_loop(W, T, loop):
-    """More than 8 ranks: the rank sum adds them one load round at a time from 8
+    """Six ranks or more: the rank sum adds them one load round at a time from 8
     workgroups per CU (2048 elements per workgroup: T*H >= 8 * 256 * 2048)."""
     rc, p = rplan(W, T, 2048)
     assert rc == A.ARRMS_OK and p["rank_loop"] == loop, p
