@@ -313,6 +313,20 @@ bool mid_ranks_rank_loop(int cu_count, int world, int tokens, int hidden, const 
     return tokens >= 8LL * cu_count;
 }
 
+// Rows the 16-byte kernels cannot take, with eight ranks: the rank loop instead of the
+// specialised 8-rank scalar instance once a row takes 512 lanes or more.  That instance
+// holds all eight ranks' loads (94 VGPRs at 2-byte loads: one 1024-lane workgroup per
+// CU), the rank loop 45 at most.  Measured on MI355X (separately allocated tensors,
+// 4.5 GB rotation): H = 8191 68.9 -> 78.1 %, H = 5119 65.3 -> 71.6 %, H = 4095 +2.6 %;
+// on 256 lanes (H = 2047) 2 % slower, and at 6 or 7 ranks 1-4 % slower, so those keep
+// the specialised instance.
+bool odd_rows_rank_loop(int cu_count, int world, int tokens, int hidden, const arrms_tuning_t* t) {
+    if (world != 8) return false;
+    if (t && (t->threads_per_row || t->scalar_elems)) return false;
+    const int lanes = ((hidden + 7) / 8 + 63) / 64 * 64;
+    return lanes >= 512 && lanes <= 1024 && tokens >= 8LL * cu_count;
+}
+
 // Widest load, in BF16 elements, that H and the OR of all pointer addresses allow.
 int scalar_elems(int hidden, uintptr_t any) {
     if (hidden % 4 == 0 && (any & 7u) == 0) return 4;
@@ -422,7 +436,8 @@ int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
             break;
     }
     if (!vector_ok) {
-        plan_scalar(world, tokens, hidden, elems, tuning, plan);
+        plan_scalar(world, tokens, hidden, elems, tuning, plan, odd_rows_rank_loop(cu_count, world, tokens, hidden,
+                                                                                    tuning));
         return ARRMS_OK;
     }
     int split_max = (tuning && tuning->splith_max_tokens >= 0) ? tuning->splith_max_tokens

@@ -100,9 +100,10 @@ int main(int argc, char** argv) {
             // the rank loop: always for the scalar kernel beyond 8 ranks; for 6-8 ranks only on
             // power-of-two workgroups with at least 8 rows per CU; never for the other variants
             if (p.variant == ARRMS_VARIANT_SCALAR && W > 8 && !p.rank_loop) return fail("fused rank loop", i);
+            const bool pow2_block = p.block == 256 || p.block == 512 || p.block == 1024;
             if (p.rank_loop && (p.variant != ARRMS_VARIANT_SCALAR ||
                                 (W <= 8 && (W < 6 || (long long)T < 8LL * cu ||
-                                            (p.block != 256 && p.block != 512 && p.block != 1024)))))
+                                            !(pow2_block || (W == 8 && p.block >= 512))))))
                 return fail("fused rank loop shape", i);
         }
         if (rc == ARRMS_OK && tp && (tp->residual_out_store < 0 || tp->residual_out_store > 2 || tp->scalar_elems == 3))

@@ -473,7 +473,14 @@ def test_scalar_rank_loop_flag():
     assert plan(12, 64, 2047)[1]["rank_loop"] == 1 and plan(8, 64, 2047)[1]["rank_loop"] == 0
     assert plan(16, 4096, 2048)[1]["rank_loop"] == 1                     # the many-ranks scalar plan
     assert plan(16, 33, 2048)[1]["rank_loop"] == 0                       # row kernel
-    assert plan(8, 4096, 2047)[1]["rank_loop"] == 0                      # odd rows: the specialised instance
+    assert plan(8, 4096, 2047)[1]["rank_loop"] == 0                      # odd rows on 256 lanes: specialised
+    # odd rows with eight ranks on 512 lanes or more, 8 rows per CU: the rank loop
+    for W, T, H, want in ((8, 4096, 4095, 1), (8, 2048, 5119, 1), (8, 2047, 5119, 0), (7, 4096, 4095, 0),
+                          (8, 4096, 8191, 1), (8, 4096, 9001, 0)):
+        rc, p = plan(W, T, H)
+        assert rc == A.ARRMS_OK and p["variant"] == A.ARRMS_VARIANT_SCALAR and p["rank_loop"] == want, (W, T, H, p)
+    t = A.arrms_tuning_t.make(scalar_elems=1)
+    assert plan(8, 4096, 4095, tuning=t)[1]["rank_loop"] == 0
 
 
 def test_scalar_lanes_tuning():

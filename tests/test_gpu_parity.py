@@ -133,7 +133,7 @@ def test_residual_out_store_policies(W, T, H, variant, store):
 # plan is the scalar kernel's rank loop.
 @pytest.mark.parametrize("W,T,H", [(12, 1024, 4096), (16, 2048, 2048), (9, 1030, 1000), (11, 1024, 2046),
                                    (12, 1024, 8192), (10, 1100, 6000), (8, 2048, 2048), (6, 2100, 4096),
-                                   (7, 2048, 8184)])
+                                   (7, 2048, 8184), (8, 2048, 4095), (8, 2049, 5119), (8, 2048, 8190)])
 def test_many_ranks_scalar_plan(W, T, H):
     plan, _ = parity(W, T, H, seed=W * 1000 + H)
     assert plan["variant"] == SCALAR
