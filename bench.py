@@ -657,6 +657,44 @@ def store_policy(ctx, tokens=(4096, 16384), rounds=2):
     return out
 
 
+def line_offset_rows(ctx, shapes=((1, 16384, 2040), (4, 4096, 6000)), rounds=3):
+    """Rows whose stride is not a multiple of 128 bytes (H % 64 != 0): the automatic plan
+    (the scalar kernel, its lanes rotated onto whole lines) against the row kernel forced.
+    Each shape on its own rotating pool (its first 256 rows of seeded inputs repeated),
+    back-to-back GPU time, the two interleaved, the best of `rounds` each."""
+    torch, A = ctx.torch, ctx.A
+    out = []
+    for W, T, H in shapes:
+        wl = ctx.synth.WORKLOADS["prefill"].with_(world=W, tokens=min(T, 256), hidden=H, seed=700 + W)
+        x, r, w = ctx.synth.make_inputs(wl)
+        lpool = Pool(torch, x, r, w, rows=T)
+        del x, r
+        lop = A.FusedReduceResidualRMSNorm(max_world=W, max_tokens=T, max_hidden=H, device=0)
+        lctx = Ctx(torch, A, ctx.synth, lop, lpool, W, H, wl.eps, ctx.stream)
+        rec = {"W": W, "T": T, "H": H}
+        best = {}
+        for _ in range(rounds):
+            for variant, name in ((A.ARRMS_VARIANT_AUTO, "auto"), (A.ARRMS_VARIANT_ROW, "row")):
+                lop.set_variant(variant)
+                rec[name + "_variant"] = VARIANT_NAMES[lctx.plan(T)["variant"]]
+                c = lctx.caller(T)
+                for _ in range(30):
+                    c()
+                _, g = time_back_to_back(torch, c, 300 if T <= 4096 else 100)
+                best[name] = min(best.get(name, 1e9), g * 1e3)
+        b = algorithmic_bytes(W, T, H)
+        for name, us in best.items():
+            rec[name + "_us"] = us
+            rec[name + "_frac_of_peak_gpu_events"] = b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
+        out.append(rec)
+        log("line-offset rows W=%d T=%d H=%d: automatic (%s) %.2f us, row kernel %.2f us" % (
+            W, T, H, rec["auto_variant"], best["auto"], best["row"]))
+        lop.close()
+        del lpool
+        torch.cuda.empty_cache()
+    return out
+
+
 def reduce_offsets(ctx, W=4, T=4096):
     """The rank sum alone at W=4 T=4096 H=2048 with its tensors placed at byte offsets:
     every tensor at the same offset (16-byte loads after a short head) and the output
@@ -1116,7 +1154,7 @@ def main():
         log("parity of the timed configuration vs oracle: %s" % parity)
 
     sweep, fit, fusion, reduce_sweep, variants, splith_regime, worlds = [], None, None, [], [], [], []
-    ceiling, scalar, reduce_offs, stores = None, [], [], []
+    ceiling, scalar, reduce_offs, stores, line_offset = None, [], [], [], []
     if not args.no_sweep:
         ctx = Ctx(torch, A, synth, op, pool, W, H, eps, stream)
         ceiling = read_ceiling(ctx, achieved)
@@ -1127,6 +1165,7 @@ def main():
         scalar = scalar_widths(ctx)
         reduce_offs = reduce_offsets(ctx)
         stores = store_policy(ctx, tokens=tuple(t for t in (4096, 16384) if t <= pool.T))
+        line_offset = line_offset_rows(ctx)
         splith_regime = splith_crossover(ctx)
         worlds = world_sweep(ctx)
 
@@ -1188,6 +1227,7 @@ def main():
         "scalar_widths": scalar,
         "reduce_offsets": reduce_offs,
         "store_policy": stores,
+        "line_offset_rows": line_offset,
         "splith_regime": splith_regime,
         "world_sweep": worlds,
         "ceiling": ceiling,

@@ -327,6 +327,25 @@ bool odd_rows_rank_loop(int cu_count, int world, int tokens, int hidden, const a
     return lanes >= 512 && lanes <= 1024 && tokens >= 8LL * cu_count;
 }
 
+// Rows whose stride is not a multiple of 128 bytes (H % 64 != 0, H % 8 == 0): row r
+// starts at byte 2*r*H mod 128 of a line, so the row kernel's wave instructions
+// straddle two cache lines in most rows, while the scalar kernel rotates its lanes
+// onto whole lines (8-byte loads here).  Measured on MI355X (4.5 GB rotation,
+// interleaved runs) for rows of one span: from 256 lanes (H > 1536) and 16 rows per
+// CU the scalar kernel is even or faster, 2-6 % at W = 2-8 (H = 2040, 3000, 5000, 6000, 8136) and 15-18 % at W = 1
+// (four vectors per lane in the row kernel), except -1.3 % at W = 4 H = 7000; with 8
+// rows per CU W = 1 lost 4 %.  Shorter rows gain only at one rank with 64 rows per CU
+// (7-22 % at H = 520-1032; even or 2 % slower with 16-32), and lose 5-15 % at W = 4,
+// where the row kernel packs several rows per workgroup.  A tuned lane layout keeps the
+// row kernel.
+bool line_offset_rows_scalar(int cu_count, int world, int tokens, int hidden, const arrms_tuning_t* t) {
+    if (hidden % 64 == 0 || hidden > 8 * 1024) return false;
+    if (t && (t->vec_per_thread || t->threads_per_row || t->rows_per_block)) return false;
+    const int lanes = ((hidden + 7) / 8 + 63) / 64 * 64;
+    if (lanes >= 256) return tokens >= 16LL * cu_count;
+    return world == 1 && tokens >= 64LL * cu_count;
+}
+
 // Widest load, in BF16 elements, that H and the OR of all pointer addresses allow.
 int scalar_elems(int hidden, uintptr_t any) {
     if (hidden % 4 == 0 && (any & 7u) == 0) return 4;
@@ -450,6 +469,11 @@ int plan_fused(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
     // Six to eight ranks on power-of-two workgroups, enough rows: its rank loop.
     if (tokens > split_max && mid_ranks_rank_loop(cu_count, world, tokens, hidden, tuning)) {
         plan_scalar(world, tokens, hidden, elems, tuning, plan, true);
+        return ARRMS_OK;
+    }
+    // Rows that start inside a 128-byte line, enough rows: the scalar kernel's rotated lanes.
+    if (tokens > split_max && line_offset_rows_scalar(cu_count, world, tokens, hidden, tuning)) {
+        plan_scalar(world, tokens, hidden, elems, tuning, plan);
         return ARRMS_OK;
     }
     // The automatic choice always finds a plan: tuning overrides that no vector

@@ -448,6 +448,31 @@ def test_mid_ranks_rank_loop(W, T, H, loop):
     assert plan(W, T, H, tuning=t)[1]["variant"] == A.ARRMS_VARIANT_ROW
 
 
+# Rows whose stride is not a multiple of 128 bytes (H % 64 != 0): the scalar kernel
+# (8-byte loads, lanes rotated onto whole lines) for rows of 256-1024 lanes from 16 rows
+# per CU, and for shorter rows at one rank from 64 rows per CU; aligned strides, longer
+# rows, fewer rows and tuned lane layouts keep the row kernel.
+@pytest.mark.parametrize("W,T,H,variant", [
+    (4, 4096, 2040, A.ARRMS_VARIANT_SCALAR), (4, 4095, 2040, A.ARRMS_VARIANT_ROW),
+    (4, 4096, 2048, A.ARRMS_VARIANT_ROW), (1, 4096, 2040, A.ARRMS_VARIANT_SCALAR),
+    (2, 16384, 6000, A.ARRMS_VARIANT_SCALAR), (4, 4096, 8136, A.ARRMS_VARIANT_SCALAR),
+    (4, 4096, 8200, A.ARRMS_VARIANT_ROW), (5, 8192, 1544, A.ARRMS_VARIANT_SCALAR),
+    (4, 16384, 1528, A.ARRMS_VARIANT_ROW), (4, 16384, 520, A.ARRMS_VARIANT_ROW),
+    (1, 16384, 1000, A.ARRMS_VARIANT_SCALAR), (1, 16383, 1000, A.ARRMS_VARIANT_ROW),
+    (2, 16384, 1000, A.ARRMS_VARIANT_ROW), (8, 8192, 3000, A.ARRMS_VARIANT_SCALAR),
+])
+def test_line_offset_rows_take_the_scalar_kernel(W, T, H, variant):
+    rc, p = plan(W, T, H)
+    assert rc == A.ARRMS_OK and p["variant"] == variant, (W, T, H, p)
+    if variant == A.ARRMS_VARIANT_SCALAR:
+        assert p["elems_per_load"] == 4 and p["rank_loop"] == 0, p
+    for t in (dict(vec_per_thread=1), dict(threads_per_row=256), dict(rows_per_block=1)):
+        rc, p = plan(W, T, H, tuning=A.arrms_tuning_t.make(**t))
+        assert rc == A.ARRMS_OK and p["variant"] == A.ARRMS_VARIANT_ROW or H > 8192, (t, p)
+    rc, p = plan(4, 2048, 2040, cu=128)                           # 16 rows per CU on 128 CUs
+    assert p["variant"] == A.ARRMS_VARIANT_SCALAR
+
+
 def test_many_ranks_rule_scales_with_cus_and_respects_tuning():
     lim = dict(LIM)
     rc, p = plan(12, 512, 2048, cu=128, lim=lim)                # 4 rows per CU on 128 CUs

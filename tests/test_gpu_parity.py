@@ -139,6 +139,15 @@ def test_many_ranks_scalar_plan(W, T, H):
     assert plan["variant"] == SCALAR
 
 
+# Rows whose stride is not a multiple of 128 bytes, with enough rows: the automatic plan
+# is the scalar kernel, 8-byte loads, lanes rotated onto whole lines row by row.
+@pytest.mark.parametrize("W,T,H", [(4, 4096, 2040), (1, 16384, 1000), (2, 4096, 6000), (8, 4096, 3000),
+                                   (5, 4100, 8136), (3, 4097, 1544)])
+def test_line_offset_rows_scalar_plan(W, T, H):
+    plan, _ = parity(W, T, H, seed=W * 1000 + H + 7)
+    assert plan["variant"] == SCALAR and plan["elems_per_load"] == 4 and plan["rank_loop"] == 0
+
+
 def _shifted(t, off, dev):
     """A copy of CPU tensor t on the GPU, starting `off` bytes past a 256-byte boundary."""
     buf = torch.zeros(t.numel() + 16, dtype=torch.bfloat16, device=dev)
