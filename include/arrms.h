@@ -141,10 +141,13 @@ int arrms_create(arrms_handle_t* out, int device, int max_world, int max_tokens,
  *   norm_out     : BF16 [tokens][hidden] output
  * Pointers must be 2-byte aligned.  Outputs may not overlap each other or any
  * input, except residual_out == residual.  Inputs may overlap each other.
- * H a multiple of 8 with every pointer 16-byte aligned uses the vector kernels;
- * anything else uses the scalar kernel with the same results, with loads of 4
- * BF16 elements when H % 4 == 0 and every pointer is 8-byte aligned, of 2 when
- * H is even and every pointer 4-byte aligned, else of 1.
+ * Only H a multiple of 8 with every pointer 16-byte aligned can use the vector
+ * kernels (the automatic choice still gives some of those calls to the scalar
+ * kernel where it measured faster: 6-16 ranks with enough rows, rows whose stride
+ * is not a multiple of 128 bytes); anything else uses the scalar kernel.  The
+ * scalar kernel gives the same results and loads 4 BF16 elements at a time when
+ * H % 4 == 0 and every pointer is 8-byte aligned, 2 when H is even and every
+ * pointer 4-byte aligned, else 1.
  * All checks happen before anything is enqueued: an error has no side effect.
  * Returns ARRMS_OK, ARRMS_ERR_INVALID_ARG, ARRMS_ERR_UNSUPPORTED (a forced
  * variant cannot run this shape, or the launch would exceed 2^32 - 1 work-items,
