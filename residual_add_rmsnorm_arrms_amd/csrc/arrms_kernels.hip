@@ -204,12 +204,14 @@ __global__ void __launch_bounds__(1024) splith_norm_kernel(const SplitNormArgs a
 
 // -------------------------------------------------------------- scalar variant
 // Rows that the 16-byte kernels cannot take (H % 8 != 0, or a pointer not 16-byte
-// aligned), and, through the generic instance's rank loop (W = 0: only x_0 loaded
-// up front, the other ranks added one load round at a time), calls with many ranks
-// that the planner gives it.  Loads are E BF16 elements wide (E = 4, 2 or 1: 8-, 4-
-// or 2-byte loads), the widest that H and the alignment of every pointer allow.  One
-// row per workgroup of n lanes (n <= 1024), XCD runs as in the row variant.  The row is walked in spans of kScalarSpan * n elements; in a
-// span lane l owns the E-element groups l, l + n, ..., l + (8 / E - 1) * n, so each
+// aligned); rows whose stride is not a multiple of 128 bytes (H % 64 != 0), which
+// the planner gives it where its line rotation (below) measured faster; and,
+// through the generic instance's rank loop (W = 0: only x_0 loaded up front, the
+// other ranks added one load round at a time), calls with many ranks.  Loads are E
+// BF16 elements wide (E = 4, 2 or 1: 8-, 4- or 2-byte loads), the widest that H and
+// the alignment of every pointer allow.  One row per workgroup of n lanes
+// (n <= 1024), XCD runs as in the row variant.  The row is walked in spans of
+// kScalarSpan * n elements; in a span lane l owns the E-element groups l, l + n, ..., l + (8 / E - 1) * n, so each
 // load instruction of a wave covers 128 * E contiguous bytes and a lane moves 16
 // bytes per input per span, as in the row variant.
 //
@@ -224,8 +226,8 @@ __global__ void __launch_bounds__(1024) splith_norm_kernel(const SplitNormArgs a
 // residual_out stays in registers for the second pass; otherwise the second pass
 // re-reads it (each group is read back by the lane that stored it).
 //
-// A row whose start is not on a 128-byte line (odd H, or a pointer offset) would
-// make every wave instruction straddle two lines.  So the lanes' group indexes are
+// A row whose start is not on a 128-byte line (H % 64 != 0, or a pointer offset)
+// would make every wave instruction straddle two lines.  So the lanes' group indexes are
 // moved back by the row's offset within its line of the first partial (`shift`
 // groups); the wave instructions then cover whole lines of every tensor aligned
 // like that partial.  A row that fits one span is rotated: index i takes group
