@@ -657,6 +657,36 @@ def store_policy(ctx, tokens=(4096, 16384), rounds=2):
     return out
 
 
+def kernarg_preload(ctx, tokens=(1024, 4096), rounds=3):
+    """Kernels with preloaded arguments (the automatic choice from 16 MiB per call)
+    against the same kernels taking one argument block (tuning kernarg_preload=1), on
+    the prefill pool's rotating buffers: back-to-back GPU time, interleaved, the best of
+    `rounds` each."""
+    torch, op = ctx.torch, ctx.op
+    out = []
+    for t in tokens:
+        best = {}
+        for _ in range(rounds):
+            for mode, name in ((0, "preloaded"), (1, "argument_block")):
+                op.set_tuning(kernarg_preload=mode)
+                c = ctx.caller(t)
+                for _ in range(30):
+                    c()
+                _, g = time_back_to_back(torch, c, 300 if t <= 4096 else 100)
+                best[name] = min(best.get(name, 1e9), g * 1e3)
+        op.set_tuning()
+        plan = ctx.plan(t)
+        b = algorithmic_bytes(ctx.W, t, ctx.H)
+        rec = {"W": ctx.W, "T": t, "H": ctx.H, "automatic_kernarg_preload": plan["kernarg_preload"]}
+        for name, us in best.items():
+            rec[name + "_us"] = us
+            rec[name + "_frac_of_peak_gpu_events"] = b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
+        out.append(rec)
+        log("kernel arguments W=%d T=%d H=%d: preloaded %.2f us, one argument block %.2f us" % (
+            ctx.W, t, ctx.H, best["preloaded"], best["argument_block"]))
+    return out
+
+
 def line_offset_rows(ctx, shapes=((1, 16384, 2040), (4, 4096, 6000)), rounds=3):
     """Rows whose stride is not a multiple of 128 bytes (H % 64 != 0): the automatic plan
     (the scalar kernel, its lanes rotated onto whole lines) against the row kernel forced.
@@ -1154,7 +1184,7 @@ def main():
         log("parity of the timed configuration vs oracle: %s" % parity)
 
     sweep, fit, fusion, reduce_sweep, variants, splith_regime, worlds = [], None, None, [], [], [], []
-    ceiling, scalar, reduce_offs, stores, line_offset = None, [], [], [], []
+    ceiling, scalar, reduce_offs, stores, line_offset, preload = None, [], [], [], [], []
     if not args.no_sweep:
         ctx = Ctx(torch, A, synth, op, pool, W, H, eps, stream)
         ceiling = read_ceiling(ctx, achieved)
@@ -1166,6 +1196,7 @@ def main():
         reduce_offs = reduce_offsets(ctx)
         stores = store_policy(ctx, tokens=tuple(t for t in (4096, 16384) if t <= pool.T))
         line_offset = line_offset_rows(ctx)
+        preload = kernarg_preload(ctx, tokens=tuple(t for t in (1024, 4096) if t <= pool.T))
         splith_regime = splith_crossover(ctx)
         worlds = world_sweep(ctx)
 
@@ -1228,6 +1259,7 @@ def main():
         "reduce_offsets": reduce_offs,
         "store_policy": stores,
         "line_offset_rows": line_offset,
+        "kernarg_preload": preload,
         "splith_regime": splith_regime,
         "world_sweep": worlds,
         "ceiling": ceiling,

@@ -87,6 +87,10 @@ typedef struct {
     int rank_loop;       /* 1: the ranks after x_0 are added one load round at a time (the scalar kernel with more
                             than 8 ranks, or chosen automatically for 6-8 ranks; the rank sum with 6 ranks or more
                             and at least 8 workgroups per CU); 0: every rank's loads are issued together */
+    int kernarg_preload; /* 1: the kernel takes its arguments as a flat list whose leading 14 dwords (sizes,
+                            residual, first partials) are preloaded into scalar registers at wave launch, so its
+                            waves start without fetching them (row, scalar and rank sum with W <= 8, calls of at
+                            least 16 MiB, where the longer host launch is hidden); 0: one argument block */
 } arrms_plan_t;
 
 /* Optional tuning overrides; 0 (or -1 where stated) keeps the automatic choice.
@@ -102,6 +106,8 @@ typedef struct {
     int scalar_elems;      /* scalar and rank sum: at most this many BF16 elements per load (1, 2 or 4); 0 automatic */
     int residual_out_store; /* row and scalar: 0 or 1 streaming stores (automatic), 2 write-back stores (faster
                                only when the call's data is cache-resident) */
+    int kernarg_preload;   /* 0 automatic; 1 never; 2 whenever the kernel has a flat twin (W <= 8, not split-H,
+                              not the rank loop) */
 } arrms_tuning_t;
 
 /*

@@ -51,7 +51,8 @@ EXPORTS = ("arrms_create", "arrms_fused", "arrms_destroy", "arrms_status_string"
 class arrms_plan_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("variant", "grid", "block", "vec_per_thread", "threads_per_row",
                                             "rows_per_block", "chunks_per_row", "kernels", "blocks", "xcd_chunk",
-                                            "elems_per_load", "residual_out_cached", "rank_loop")]
+                                            "elems_per_load", "residual_out_cached", "rank_loop",
+                                            "kernarg_preload")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -60,13 +61,13 @@ class arrms_plan_t(ctypes.Structure):
 class arrms_tuning_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("vec_per_thread", "threads_per_row", "splith_block",
                                             "splith_max_tokens", "xcd_chunk", "rows_per_block", "scalar_elems",
-                                            "residual_out_store")]
+                                            "residual_out_store", "kernarg_preload")]
 
     @classmethod
     def make(cls, vec_per_thread=0, threads_per_row=0, splith_block=0, splith_max_tokens=-1, xcd_chunk=-1,
-             rows_per_block=0, scalar_elems=0, residual_out_store=0):
+             rows_per_block=0, scalar_elems=0, residual_out_store=0, kernarg_preload=0):
         return cls(vec_per_thread, threads_per_row, splith_block, splith_max_tokens, xcd_chunk, rows_per_block,
-                   scalar_elems, residual_out_store)
+                   scalar_elems, residual_out_store, kernarg_preload)
 
 
 class ArrmsError(RuntimeError):

@@ -2,7 +2,8 @@
 
 The library is always compiled for gfx950 only.  Floating-point flags keep the
 kernels' arithmetic plain IEEE: no fast-math, no FMA contraction, binary32
-denormals kept, and packed binary32 instructions disabled.
+denormals kept, and packed binary32 instructions disabled.  Kernel arguments passed
+as a flat list of scalars are preloaded into scalar registers.
 """
 from __future__ import annotations
 
@@ -23,6 +24,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wextra",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
+    # kernels whose arguments are a flat list of scalars get the leading 14 dwords
+    # preloaded into scalar registers at wave launch (a no-op for by-value blocks)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

@@ -97,6 +97,7 @@ bool valid_tuning(const arrms_tuning_t* t) {
     const int se = t->scalar_elems;
     if (!(se == 0 || se == 1 || se == 2 || se == 4)) return false;
     if (t->residual_out_store < 0 || t->residual_out_store > 2) return false;
+    if (t->kernarg_preload < 0 || t->kernarg_preload > 2) return false;
     return true;
 }
 
@@ -564,6 +565,23 @@ int plan_reduce(int cu_count, const arrms_tuning_t* tuning, int max_world, int m
     return ARRMS_OK;
 }
 
+// Kernels with preloaded arguments (plan field kernarg_preload): their waves start
+// without fetching the argument block from memory.  Measured on MI355X (W=4 H=2048,
+// rotating buffers, the two interleaved): T = 1024 5 % faster, T = 4096 1.8 %
+// (20.5 against 20.9 us), T = 16384 0.3 %; in HIP-graph replay T = 1 and 64 4-6 %
+// faster.  Their flat argument list costs the host 0.2 us more per launch, and in
+// some processes about 1 us more (back-to-back calls from C at T = 1 and 16 took
+// 3.5-3.8 us instead of 2.5-2.7), so they serve only calls whose GPU time hides the
+// launch: at least 16 MiB of traffic (about 5 us per call at W=4 H=2048).  Only row, scalar and
+// rank-sum kernels specialised on W <= 8 have such twins (not split-H, which serves
+// decode sizes, nor the rank loop's generic kernels, which carry 16 pointers).
+constexpr long long kPreloadMinBytes = 16LL << 20;
+
+void choose_preload(const arrms_tuning_t* t, bool has_twin, long long bytes, arrms_plan_t* p) {
+    const int mode = t ? t->kernarg_preload : 0;
+    p->kernarg_preload = has_twin && (mode == 2 || (mode == 0 && bytes >= kPreloadMinBytes)) ? 1 : 0;
+}
+
 }  // namespace
 
 namespace arrms {
@@ -594,6 +612,7 @@ hipError_t launch_fused(const arrms_plan_t& p, const void* const* partials, int 
     a.elems_per_load = p.elems_per_load;
     a.ro_cached = p.residual_out_cached;
     a.rank_loop = p.rank_loop;
+    a.preload = p.kernarg_preload;
     switch (p.variant) {
         case ARRMS_VARIANT_ROW: return launch_row(a, p.vec_per_thread, p.grid, p.block, stream);
         case ARRMS_VARIANT_SPLITH: return launch_splith(a, p.vec_per_thread, p.grid, p.block, stream);
@@ -610,17 +629,26 @@ int arrms_plan(int cu_count, int variant, const arrms_tuning_t* tuning, int max_
                int max_hidden, const void* const* partials, int world, int tokens, int hidden,
                const void* residual, const void* weight, float eps, const void* residual_out,
                const void* norm_out, arrms_plan_t* plan) {
-    return check_grid(plan_fused(cu_count, variant, tuning, max_world, max_tokens, max_hidden, partials, world,
-                                 tokens, hidden, residual, weight, eps, residual_out, norm_out, plan),
-                      plan);
+    const int rc = check_grid(plan_fused(cu_count, variant, tuning, max_world, max_tokens, max_hidden, partials,
+                                         world, tokens, hidden, residual, weight, eps, residual_out, norm_out, plan),
+                              plan);
+    if (rc == ARRMS_OK && plan->grid > 0) {
+        const bool twin = world <= 8 && (plan->variant == ARRMS_VARIANT_ROW ||
+                                         (plan->variant == ARRMS_VARIANT_SCALAR && !plan->rank_loop));
+        choose_preload(tuning, twin, 2LL * tokens * hidden * (world + 3) + 2LL * hidden, plan);
+    }
+    return rc;
 }
 
 int arrms_plan_reduce(int cu_count, const arrms_tuning_t* tuning, int max_world, int max_tokens, int max_hidden,
                       const void* const* partials, int world, int tokens, int hidden, const void* reduced,
                       arrms_plan_t* plan) {
-    return check_grid(plan_reduce(cu_count, tuning, max_world, max_tokens, max_hidden, partials, world, tokens,
-                                  hidden, reduced, plan),
-                      plan);
+    const int rc = check_grid(plan_reduce(cu_count, tuning, max_world, max_tokens, max_hidden, partials, world,
+                                          tokens, hidden, reduced, plan),
+                              plan);
+    if (rc == ARRMS_OK && plan->grid > 0)
+        choose_preload(tuning, world <= 8 && !plan->rank_loop, 2LL * tokens * hidden * (world + 1), plan);
+    return rc;
 }
 
 int arrms_reduce(arrms_handle_t h, const void* const* partials, int world, int tokens, int hidden, void* reduced,
@@ -645,6 +673,7 @@ int arrms_reduce(arrms_handle_t h, const void* const* partials, int world, int t
     a.head = head;
     a.elems_per_load = elems;
     a.rank_loop = p.rank_loop;
+    a.preload = p.kernarg_preload;
     a.blocks = p.blocks;
     a.xcd_chunk = p.xcd_chunk;
     int prev = -1;

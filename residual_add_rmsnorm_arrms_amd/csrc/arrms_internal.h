@@ -44,6 +44,8 @@ struct Args {
     int head;               // rank sum only: elements before the aligned start of x.p[] / reduced
     int ro_cached;          // row, scalar: 1 write-back stores for residual_out, 0 streaming stores
     int rank_loop;          // rank sum, scalar: 1 add the ranks after x_0 one load round at a time
+    int preload;            // row, scalar, rank sum with W <= 8: 1 launch the kernels whose leading
+                            // arguments the dispatcher preloads into scalar registers
     long long count;        // rank sum only: elements from the aligned start (tokens * hidden - head)
 };
 
@@ -147,6 +149,58 @@ inline Ptrs<WA> pack_ptrs(const Args& a) {
 template <typename K>
 inline hipError_t launch_with(const void* fn, const K& args, int grid, int block, hipStream_t s) {
     void* p[] = {const_cast<K*>(&args)};
+    return hipLaunchKernel(fn, dim3(grid), dim3(block), p, 0, s);
+}
+
+// ------------------------------------------------- preloaded argument lists
+// gfx950 can preload the first 14 dwords of a kernel's arguments into scalar
+// registers when it launches a wave, but only arguments passed as scalars (not an
+// aggregate passed by value).  A wave of the kernels above first waits for its
+// argument block to arrive from memory; the twins below take their arguments as a
+// flat list whose leading 14 dwords are what a wave needs first (sizes, the
+// residual and the first four partial pointers), so their waves start without
+// that round trip.  Each twin receives the same values as its by-value original
+// and rebuilds the same argument block, so the two compute the same bits.  The
+// flat list costs the host more per launch, so the planner takes the twins only
+// for calls long enough to hide that (arrms_plan_t::kernarg_preload).
+//
+// Host copy of the flat list of the row and scalar twins, in parameter order:
+// 4 + 2 + 8 * 2 + 3 * 2 = 28 dwords, 112 bytes; partials past W are null.
+struct FlatFusedArgs {
+    int tokens;
+    int xcd_chunk;
+    uint32_t shape;
+    float eps;
+    const void* residual;
+    const void* x[8];
+    const void* weight;
+    void* residual_out;
+    void* norm_out;
+};
+
+// Host copy of the flat list of the rank-sum twins: 4 + 2 + 8 * 2 + 2 = 24
+// dwords, 96 bytes; the output pointer last, so that the first four partials are
+// among the preloaded dwords.
+struct FlatReduceArgs {
+    int blocks;
+    int xcd_chunk;
+    int world;
+    int head;
+    long long count;
+    const void* x[8];
+    void* reduced;
+};
+
+// Launch `fn` with the fields of a flat argument list, one kernel parameter each.
+inline hipError_t launch_flat(const void* fn, FlatFusedArgs& f, int grid, int block, hipStream_t s) {
+    void* p[] = {&f.tokens, &f.xcd_chunk, &f.shape, &f.eps, &f.residual, &f.x[0], &f.x[1], &f.x[2],
+                 &f.x[3], &f.x[4], &f.x[5], &f.x[6], &f.x[7], &f.weight, &f.residual_out, &f.norm_out};
+    return hipLaunchKernel(fn, dim3(grid), dim3(block), p, 0, s);
+}
+
+inline hipError_t launch_flat(const void* fn, FlatReduceArgs& f, int grid, int block, hipStream_t s) {
+    void* p[] = {&f.blocks, &f.xcd_chunk, &f.world, &f.head, &f.count, &f.x[0], &f.x[1], &f.x[2],
+                 &f.x[3], &f.x[4], &f.x[5], &f.x[6], &f.x[7], &f.reduced};
     return hipLaunchKernel(fn, dim3(grid), dim3(block), p, 0, s);
 }
 

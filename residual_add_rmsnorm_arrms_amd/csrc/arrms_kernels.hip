@@ -47,8 +47,34 @@ constexpr int row_max_threads() {
     return (W == 0 || W > 8) ? (VPT == 1 ? 512 : 256) : (VPT == 1 ? 1024 : (VPT <= 4 ? 512 : 256));
 }
 
+// The flat argument list of the row and scalar twins (FlatFusedArgs on the host),
+// and the argument block rebuilt from it.
+#define ARRMS_FLAT_FUSED_PARAMS                                                                              \
+    int tokens, int xcd_chunk, uint32_t shape, float eps, const void* residual, const void* x0, const void* x1, \
+        const void* x2, const void* x3, const void* x4, const void* x5, const void* x6, const void* x7,          \
+        const void* weight, void* residual_out, void* norm_out
+#define ARRMS_FLAT_FUSED_NAMES \
+    tokens, xcd_chunk, shape, eps, residual, x0, x1, x2, x3, x4, x5, x6, x7, weight, residual_out, norm_out
+
+template <class K, int W>
+__device__ __forceinline__ K fused_block(ARRMS_FLAT_FUSED_PARAMS) {
+    const void* const x[8] = {x0, x1, x2, x3, x4, x5, x6, x7};
+    K a;
+#pragma unroll
+    for (int r = 0; r < W; ++r) a.x.p[r] = x[r];
+    a.residual = residual;
+    a.weight = weight;
+    a.residual_out = residual_out;
+    a.norm_out = norm_out;
+    a.eps = eps;
+    a.tokens = tokens;
+    a.xcd_chunk = xcd_chunk;
+    a.shape = shape;
+    return a;
+}
+
 template <int W, int VPT, bool RC>
-__global__ void __launch_bounds__((row_max_threads<W, VPT>())) row_kernel(const RowArgs<(W > 0 ? W : kMaxWorld)> a) {
+__device__ __forceinline__ void row_body(const RowArgs<(W > 0 ? W : kMaxWorld)>& a) {
     constexpr int WA = W > 0 ? W : kMaxWorld;
     const int world = W > 0 ? W : static_cast<int>((a.shape >> 26) & 31u);
     const int nvec = static_cast<int>(a.shape & 0xffffu);
@@ -112,6 +138,19 @@ __global__ void __launch_bounds__((row_max_threads<W, VPT>())) row_kernel(const 
 #pragma unroll
     for (int k = 0; k < VPT; ++k)
         if (ok[k]) st4_stream(a.norm_out, base + lane + k * tpr, norm_vec(ro[k], inv, wv[k]));
+}
+
+template <int W, int VPT, bool RC>
+__global__ void __launch_bounds__((row_max_threads<W, VPT>())) row_kernel(const RowArgs<(W > 0 ? W : kMaxWorld)> a) {
+    row_body<W, VPT, RC>(a);
+}
+
+// The same kernel for W <= 8 with the flat argument list, its leading dwords
+// preloaded into scalar registers.
+template <int W, int VPT, bool RC>
+__global__ void __launch_bounds__((row_max_threads<W, VPT>())) row_kernel_flat(ARRMS_FLAT_FUSED_PARAMS) {
+    static_assert(W >= 1 && W <= 8, "flat argument lists carry at most 8 partials");
+    row_body<W, VPT, RC>(fused_block<RowArgs<W>, W>(ARRMS_FLAT_FUSED_NAMES));
 }
 
 // ------------------------------------------------------------ split-H variant
@@ -248,7 +287,7 @@ template <int W>
 constexpr int scalar_max_threads() { return 1024; }
 
 template <int W, int E, bool RC>
-__global__ void __launch_bounds__(scalar_max_threads<W>()) scalar_kernel(const ScalarArgs<(W > 0 ? W : kMaxWorld)> a) {
+__device__ __forceinline__ void scalar_body(const ScalarArgs<(W > 0 ? W : kMaxWorld)>& a) {
     typedef typename Group<E>::T G;
     typedef Buf<E> B;
     constexpr int S = kScalarSpan / E;  // groups per lane per input in a span
@@ -376,6 +415,18 @@ __global__ void __launch_bounds__(scalar_max_threads<W>()) scalar_kernel(const S
     }
 }
 
+template <int W, int E, bool RC>
+__global__ void __launch_bounds__(scalar_max_threads<W>()) scalar_kernel(const ScalarArgs<(W > 0 ? W : kMaxWorld)> a) {
+    scalar_body<W, E, RC>(a);
+}
+
+// The same kernel for W <= 8 with the flat argument list (leading dwords preloaded).
+template <int W, int E, bool RC>
+__global__ void __launch_bounds__(scalar_max_threads<W>()) scalar_kernel_flat(ARRMS_FLAT_FUSED_PARAMS) {
+    static_assert(W >= 1 && W <= 8, "flat argument lists carry at most 8 partials");
+    scalar_body<W, E, RC>(fused_block<ScalarArgs<W>, W>(ARRMS_FLAT_FUSED_NAMES));
+}
+
 // ---------------------------------------------------------------- launchers
 // Argument blocks.  Each returns false when a size does not fit its packed
 // field (the planner never produces such a plan; the launch is then refused).
@@ -401,10 +452,32 @@ bool row_args(const Args& a, RowArgs<WA>* r) {
     return true;
 }
 
+// The flat argument list of the row and scalar twins, from their argument block.
+template <int WA, class K>
+FlatFusedArgs flat_fused(const K& r) {
+    FlatFusedArgs f{};
+    f.tokens = r.tokens;
+    f.xcd_chunk = r.xcd_chunk;
+    f.shape = r.shape;
+    f.eps = r.eps;
+    f.residual = r.residual;
+    for (int i = 0; i < WA && i < 8; ++i) f.x[i] = r.x.p[i];
+    f.weight = r.weight;
+    f.residual_out = r.residual_out;
+    f.norm_out = r.norm_out;
+    return f;
+}
+
+// `fn` is the flat twin when a.preload is set (W <= 8), else the by-value kernel.
 template <int WA>
 hipError_t launch_row_with(const void* fn, const Args& a, int grid, int block, hipStream_t s) {
     RowArgs<WA> r;
     if (!row_args<WA>(a, &r)) return hipErrorInvalidValue;
+    if (a.preload) {
+        if (WA > 8) return hipErrorInvalidValue;
+        FlatFusedArgs f = flat_fused<WA>(r);
+        return launch_flat(fn, f, grid, block, s);
+    }
     return launch_with(fn, r, grid, block, s);
 }
 
@@ -444,33 +517,49 @@ hipError_t launch_scalar_with(const void* fn, const Args& a, int grid, int block
     r.xcd_chunk = a.xcd_chunk;
     r.shape = static_cast<uint32_t>(a.hidden) | static_cast<uint32_t>(block / 64) << 17 |
               static_cast<uint32_t>(a.world) << 22 | static_cast<uint32_t>(e_code) << 27;
+    if (a.preload) {
+        if (WA > 8) return hipErrorInvalidValue;
+        FlatFusedArgs f = flat_fused<WA>(r);
+        return launch_flat(fn, f, grid, block, s);
+    }
     return launch_with(fn, r, grid, block, s);
+}
+
+// The by-value kernel, or its flat twin (W <= 8 only; nullptr for other W).
+template <int W, int VPT, bool RC>
+const void* row_sym(bool flat) {
+    if constexpr (W >= 1 && W <= 8) {
+        if (flat) return reinterpret_cast<const void*>(&row_kernel_flat<W, VPT, RC>);
+    } else {
+        if (flat) return nullptr;
+    }
+    return reinterpret_cast<const void*>(&row_kernel<W, VPT, RC>);
 }
 
 // Instantiated (W, VPT) pairs: those whose (W + 2) * VPT live vectors fit the
 // register budget the host planner allows (40); others are never planned.
 template <int VPT, bool RC>
-const void* row_fn(int world) {
+const void* row_fn(int world, bool flat) {
     if (VPT == 8 && world > 3) return nullptr;
     switch (world) {
-        case 1: return reinterpret_cast<const void*>(&row_kernel<1, VPT, RC>);
-        case 2: return reinterpret_cast<const void*>(&row_kernel<2, VPT, RC>);
-        case 3: return reinterpret_cast<const void*>(&row_kernel<3, VPT, RC>);
+        case 1: return row_sym<1, VPT, RC>(flat);
+        case 2: return row_sym<2, VPT, RC>(flat);
+        case 3: return row_sym<3, VPT, RC>(flat);
         default: break;
     }
     if constexpr (VPT <= 4) {
         switch (world) {
-            case 4: return reinterpret_cast<const void*>(&row_kernel<4, VPT, RC>);
-            case 5: return reinterpret_cast<const void*>(&row_kernel<5, VPT, RC>);
-            case 6: return reinterpret_cast<const void*>(&row_kernel<6, VPT, RC>);
-            case 7: return reinterpret_cast<const void*>(&row_kernel<7, VPT, RC>);
-            case 8: return reinterpret_cast<const void*>(&row_kernel<8, VPT, RC>);
+            case 4: return row_sym<4, VPT, RC>(flat);
+            case 5: return row_sym<5, VPT, RC>(flat);
+            case 6: return row_sym<6, VPT, RC>(flat);
+            case 7: return row_sym<7, VPT, RC>(flat);
+            case 8: return row_sym<8, VPT, RC>(flat);
             default: break;
         }
     }
     if constexpr (VPT <= 2) {
-        if (world == 16) return reinterpret_cast<const void*>(&row_kernel<16, VPT, RC>);
-        return reinterpret_cast<const void*>(&row_kernel<0, VPT, RC>);
+        if (world == 16) return row_sym<16, VPT, RC>(flat);
+        return row_sym<0, VPT, RC>(flat);
     }
     return nullptr;
 }
@@ -500,11 +589,12 @@ const void* splith_fn(int world) {
 hipError_t launch_row(const Args& a, int vpt, int grid, int block, hipStream_t s) {
     const void* fn = nullptr;
     const bool rc = a.ro_cached != 0;
+    const bool flat = a.preload != 0;
     switch (vpt) {
-        case 1: fn = rc ? row_fn<1, true>(a.world) : row_fn<1, false>(a.world); break;
-        case 2: fn = rc ? row_fn<2, true>(a.world) : row_fn<2, false>(a.world); break;
-        case 4: fn = rc ? row_fn<4, true>(a.world) : row_fn<4, false>(a.world); break;
-        case 8: fn = rc ? row_fn<8, true>(a.world) : row_fn<8, false>(a.world); break;
+        case 1: fn = rc ? row_fn<1, true>(a.world, flat) : row_fn<1, false>(a.world, flat); break;
+        case 2: fn = rc ? row_fn<2, true>(a.world, flat) : row_fn<2, false>(a.world, flat); break;
+        case 4: fn = rc ? row_fn<4, true>(a.world, flat) : row_fn<4, false>(a.world, flat); break;
+        case 8: fn = rc ? row_fn<8, true>(a.world, flat) : row_fn<8, false>(a.world, flat); break;
         default: return hipErrorInvalidValue;
     }
     if (!fn) return hipErrorInvalidValue;
@@ -523,6 +613,7 @@ hipError_t launch_row(const Args& a, int vpt, int grid, int block, hipStream_t s
 }
 
 hipError_t launch_splith(const Args& a, int vpt, int grid, int block, hipStream_t s) {
+    if (a.preload) return hipErrorInvalidValue;  // split-H has no flat twins (decode sizes only)
     const void* fn = nullptr;
     switch (vpt) {
         case 1: fn = splith_fn<1>(a.world); break;
@@ -556,18 +647,28 @@ hipError_t launch_splith(const Args& a, int vpt, int grid, int block, hipStream_
     return launch_with(reinterpret_cast<const void*>(&splith_norm_kernel), n, grid, block, s);
 }
 
+template <int W, int E, bool RC>
+const void* scalar_sym(bool flat) {
+    if constexpr (W >= 1 && W <= 8) {
+        if (flat) return reinterpret_cast<const void*>(&scalar_kernel_flat<W, E, RC>);
+    } else {
+        if (flat) return nullptr;
+    }
+    return reinterpret_cast<const void*>(&scalar_kernel<W, E, RC>);
+}
+
 template <int E, bool RC>
-const void* scalar_fn(int world) {
+const void* scalar_fn(int world, bool flat) {
     switch (world) {
-        case 1: return reinterpret_cast<const void*>(&scalar_kernel<1, E, RC>);
-        case 2: return reinterpret_cast<const void*>(&scalar_kernel<2, E, RC>);
-        case 3: return reinterpret_cast<const void*>(&scalar_kernel<3, E, RC>);
-        case 4: return reinterpret_cast<const void*>(&scalar_kernel<4, E, RC>);
-        case 5: return reinterpret_cast<const void*>(&scalar_kernel<5, E, RC>);
-        case 6: return reinterpret_cast<const void*>(&scalar_kernel<6, E, RC>);
-        case 7: return reinterpret_cast<const void*>(&scalar_kernel<7, E, RC>);
-        case 8: return reinterpret_cast<const void*>(&scalar_kernel<8, E, RC>);
-        default: return reinterpret_cast<const void*>(&scalar_kernel<0, E, RC>);
+        case 1: return scalar_sym<1, E, RC>(flat);
+        case 2: return scalar_sym<2, E, RC>(flat);
+        case 3: return scalar_sym<3, E, RC>(flat);
+        case 4: return scalar_sym<4, E, RC>(flat);
+        case 5: return scalar_sym<5, E, RC>(flat);
+        case 6: return scalar_sym<6, E, RC>(flat);
+        case 7: return scalar_sym<7, E, RC>(flat);
+        case 8: return scalar_sym<8, E, RC>(flat);
+        default: return scalar_sym<0, E, RC>(flat);
     }
 }
 
@@ -576,12 +677,14 @@ hipError_t launch_scalar(const Args& a, int grid, int block, hipStream_t s) {
     const bool rc = a.ro_cached != 0;
     // the rank loop is the generic instance (any rank count, ranks after x_0 added one at a time)
     const int w = a.rank_loop ? 0 : a.world;
+    const bool flat = a.preload != 0;
     switch (a.elems_per_load) {
-        case 1: fn = rc ? scalar_fn<1, true>(w) : scalar_fn<1, false>(w); break;
-        case 2: fn = rc ? scalar_fn<2, true>(w) : scalar_fn<2, false>(w); break;
-        case 4: fn = rc ? scalar_fn<4, true>(w) : scalar_fn<4, false>(w); break;
+        case 1: fn = rc ? scalar_fn<1, true>(w, flat) : scalar_fn<1, false>(w, flat); break;
+        case 2: fn = rc ? scalar_fn<2, true>(w, flat) : scalar_fn<2, false>(w, flat); break;
+        case 4: fn = rc ? scalar_fn<4, true>(w, flat) : scalar_fn<4, false>(w, flat); break;
         default: return hipErrorInvalidValue;
     }
+    if (!fn) return hipErrorInvalidValue;
     if (a.rank_loop) return launch_scalar_with<kMaxWorld>(fn, a, grid, block, s);
     switch (a.world) {
         case 1: return launch_scalar_with<1>(fn, a, grid, block, s);

@@ -31,7 +31,7 @@ constexpr int kReduceLanes = 256;
 // for a load past them and drops such a store, so no group index is clamped or
 // branched on, and one 32-bit offset per group serves every tensor.
 template <int W, int L, int E>
-__global__ void __launch_bounds__(kReduceLanes) reduce_kernel(const ReduceArgs<(W > 0 ? W : kMaxWorld)> a) {
+__device__ __forceinline__ void reduce_body(const ReduceArgs<(W > 0 ? W : kMaxWorld)>& a) {
     typedef typename Group<E>::T G;
     typedef Buf<E> B;
     constexpr int WA = W > 0 ? W : kMaxWorld;
@@ -82,6 +82,31 @@ __global__ void __launch_bounds__(kReduceLanes) reduce_kernel(const ReduceArgs<(
             static_cast<uint16_t*>(a.reduced)[e] = cvt1(acc);
         }
     }
+}
+
+template <int W, int L, int E>
+__global__ void __launch_bounds__(kReduceLanes) reduce_kernel(const ReduceArgs<(W > 0 ? W : kMaxWorld)> a) {
+    reduce_body<W, L, E>(a);
+}
+
+// The same kernel for W <= 8 with a flat argument list (FlatReduceArgs on the host),
+// whose leading dwords are preloaded into scalar registers.
+template <int W, int L, int E>
+__global__ void __launch_bounds__(kReduceLanes) reduce_kernel_flat(
+    int blocks, int xcd_chunk, int world, int head, long long count, const void* x0, const void* x1, const void* x2,
+    const void* x3, const void* x4, const void* x5, const void* x6, const void* x7, void* reduced) {
+    static_assert(W >= 1 && W <= 8, "flat argument lists carry at most 8 partials");
+    const void* const x[8] = {x0, x1, x2, x3, x4, x5, x6, x7};
+    ReduceArgs<W> a;
+#pragma unroll
+    for (int r = 0; r < W; ++r) a.x.p[r] = x[r];
+    a.reduced = reduced;
+    a.count = count;
+    a.blocks = blocks;
+    a.xcd_chunk = xcd_chunk;
+    a.world = world;
+    a.head = head;
+    reduce_body<W, L, E>(a);
 }
 
 // The same sum for six ranks or more with the ranks added one load round at a time:
@@ -140,21 +165,30 @@ __global__ void __launch_bounds__(kReduceLanes) reduce_loop_kernel(const ReduceA
     }
 }
 
+template <int W, int L, int E>
+const void* reduce_sym(bool flat) {
+    return flat ? reinterpret_cast<const void*>(&reduce_kernel_flat<W, L, E>)
+                : reinterpret_cast<const void*>(&reduce_kernel<W, L, E>);
+}
+
+// The by-value kernel, or its flat twin (W <= 8 only; nullptr for more ranks).
 template <int L, int E>
-const void* reduce_fn(int world) {
+const void* reduce_fn(int world, bool flat) {
     switch (world) {
-        case 1: return reinterpret_cast<const void*>(&reduce_kernel<1, L, E>);
-        case 2: return reinterpret_cast<const void*>(&reduce_kernel<2, L, E>);
-        case 3: return reinterpret_cast<const void*>(&reduce_kernel<3, L, E>);
-        case 4: return reinterpret_cast<const void*>(&reduce_kernel<4, L, E>);
-        case 5: return reinterpret_cast<const void*>(&reduce_kernel<5, L, E>);
-        case 6: return reinterpret_cast<const void*>(&reduce_kernel<6, L, E>);
-        case 7: return reinterpret_cast<const void*>(&reduce_kernel<7, L, E>);
-        case 8: return reinterpret_cast<const void*>(&reduce_kernel<8, L, E>);
+        case 1: return reduce_sym<1, L, E>(flat);
+        case 2: return reduce_sym<2, L, E>(flat);
+        case 3: return reduce_sym<3, L, E>(flat);
+        case 4: return reduce_sym<4, L, E>(flat);
+        case 5: return reduce_sym<5, L, E>(flat);
+        case 6: return reduce_sym<6, L, E>(flat);
+        case 7: return reduce_sym<7, L, E>(flat);
+        case 8: return reduce_sym<8, L, E>(flat);
         default: break;
     }
     // more than 8 ranks: one 16 bytes' worth of groups per lane (register budget)
-    if constexpr (L * E == 8) return reinterpret_cast<const void*>(&reduce_kernel<0, L, E>);
+    if constexpr (L * E == 8) {
+        if (!flat) return reinterpret_cast<const void*>(&reduce_kernel<0, L, E>);
+    }
     return nullptr;
 }
 
@@ -168,6 +202,18 @@ hipError_t launch_reduce_with(const void* fn, const Args& a, int grid, hipStream
     r.xcd_chunk = a.xcd_chunk;
     r.world = a.world;
     r.head = a.head;
+    if (a.preload) {  // `fn` is the flat twin
+        if (WA > 8) return hipErrorInvalidValue;
+        FlatReduceArgs f{};
+        f.blocks = r.blocks;
+        f.xcd_chunk = r.xcd_chunk;
+        f.world = r.world;
+        f.head = r.head;
+        f.count = r.count;
+        for (int i = 0; i < WA && i < 8; ++i) f.x[i] = r.x.p[i];
+        f.reduced = r.reduced;
+        return launch_flat(fn, f, grid, kReduceLanes, s);
+    }
     return launch_with(fn, r, grid, kReduceLanes, s);
 }
 
@@ -176,6 +222,7 @@ hipError_t launch_reduce_with(const void* fn, const Args& a, int grid, hipStream
 hipError_t launch_reduce(const Args& a, int vpt, int grid, int block, hipStream_t s) {
     const void* fn = nullptr;
     if (a.rank_loop) {
+        if (a.preload) return hipErrorInvalidValue;  // the loop kernel serves any rank count: no flat twin
         switch (a.elems_per_load) {
             case 8: fn = reinterpret_cast<const void*>(&reduce_loop_kernel<1, 8>); break;
             case 4: fn = reinterpret_cast<const void*>(&reduce_loop_kernel<2, 4>); break;
@@ -186,18 +233,19 @@ hipError_t launch_reduce(const Args& a, int vpt, int grid, int block, hipStream_
         if (vpt > 1 || block != kReduceLanes || a.head < 0 || a.head >= a.elems_per_load) return hipErrorInvalidValue;
         return launch_reduce_with<kMaxWorld>(fn, a, grid, s);
     }
+    const bool flat = a.preload != 0;
     switch (a.elems_per_load) {
         case 8:
             switch (vpt) {
-                case 1: fn = reduce_fn<1, 8>(a.world); break;
-                case 2: fn = reduce_fn<2, 8>(a.world); break;
-                case 4: fn = reduce_fn<4, 8>(a.world); break;
+                case 1: fn = reduce_fn<1, 8>(a.world, flat); break;
+                case 2: fn = reduce_fn<2, 8>(a.world, flat); break;
+                case 4: fn = reduce_fn<4, 8>(a.world, flat); break;
                 default: return hipErrorInvalidValue;
             }
             break;
-        case 4: fn = reduce_fn<2, 4>(a.world); break;
-        case 2: fn = reduce_fn<4, 2>(a.world); break;
-        case 1: fn = reduce_fn<8, 1>(a.world); break;
+        case 4: fn = reduce_fn<2, 4>(a.world, flat); break;
+        case 2: fn = reduce_fn<4, 2>(a.world, flat); break;
+        case 1: fn = reduce_fn<8, 1>(a.world, flat); break;
         default: return hipErrorInvalidValue;
     }
     if (!fn || block != kReduceLanes || a.head < 0 || a.head >= a.elems_per_load) return hipErrorInvalidValue;

@@ -50,8 +50,9 @@ int main(int argc, char** argv) {
         const int trpb[] = {0, 0, 0, 1, 2, 3, 4, 8, 64, 128};
         const int tse[] = {0, 0, 1, 2, 4, 3};
         const int tro[] = {0, 0, 0, 1, 2, 3, -1};
+        const int tpl[] = {0, 0, 0, 1, 2, 3, -1};
         arrms_tuning_t tun = {pick(tvpt, 8), pick(ttpr, 13), pick(tblk, 7), pick(tspl, 6), pick(txcd, 8), pick(trpb, 10),
-                              pick(tse, 6), pick(tro, 7)};
+                              pick(tse, 6), pick(tro, 7), pick(tpl, 7)};
         const arrms_tuning_t* tp = (next() % 3) ? &tun : nullptr;
         const int variant = (int)(next() % 6) - 1;
         const uintptr_t base = 0x7f0000000000ull;
@@ -105,8 +106,17 @@ int main(int argc, char** argv) {
                                 (W <= 8 && (W < 6 || (long long)T < 8LL * cu ||
                                             !(pow2_block || (W == 8 && p.block >= 512))))))
                 return fail("fused rank loop shape", i);
+            // preloaded arguments: only kernels with a flat twin (row, or scalar without the rank
+            // loop, W <= 8); never when tuned off; always when tuned on; else from 16 MiB per call
+            const bool twin = W <= 8 && (p.variant == ARRMS_VARIANT_ROW ||
+                                         (p.variant == ARRMS_VARIANT_SCALAR && !p.rank_loop));
+            const long long bytes = 2LL * T * H * (W + 3) + 2LL * H;
+            const int mode = tp ? tp->kernarg_preload : 0;
+            const int want_pl = twin && (mode == 2 || (mode == 0 && bytes >= (16LL << 20)));
+            if (p.kernarg_preload != want_pl) return fail("fused kernarg preload", i);
         }
-        if (rc == ARRMS_OK && tp && (tp->residual_out_store < 0 || tp->residual_out_store > 2 || tp->scalar_elems == 3))
+        if (rc == ARRMS_OK && tp && (tp->residual_out_store < 0 || tp->residual_out_store > 2 || tp->scalar_elems == 3 ||
+                                     tp->kernarg_preload < 0 || tp->kernarg_preload > 2))
             return fail("invalid tuning accepted", i);
         // The no-allocation entry point's plan (automatic, no tuning, absolute limits):
         // every plan it accepts keeps the split-H workspace index, row * chunks + chunk
@@ -134,6 +144,10 @@ int main(int argc, char** argv) {
             if (p.variant != ARRMS_VARIANT_REDUCE && p.variant != ARRMS_VARIANT_REDUCE_SCALAR)
                 return fail("reduce variant kind", i);
             if (p.rank_loop != (W >= 6 && (long long)p.blocks >= 8LL * cu)) return fail("reduce rank loop", i);
+            const int rmode = tp ? tp->kernarg_preload : 0;
+            const int rwant = W <= 8 && !p.rank_loop &&
+                              (rmode == 2 || (rmode == 0 && 2LL * count * (W + 1) >= (16LL << 20)));
+            if (p.kernarg_preload != rwant) return fail("reduce kernarg preload", i);
             // every pointer has the same offset modulo 2E bytes, and the groups cover the elements
             int e2 = 0, head = -1;
             arrms::reduce_alignment(parts, W, no, count, e, &e2, &head);

@@ -305,11 +305,11 @@ def test_measured_automatic_choices(W, T, H, variant, vpt, tpr, k):
     assert (p["variant"], p["vec_per_thread"], p["threads_per_row"], p["xcd_chunk"]) == (variant, vpt, tpr, k)
 
 
-def rplan(W, T, H, lim=LIM, **over):
+def rplan(W, T, H, lim=LIM, tuning=None, **over):
     b = bufs(W, T, H)
     b.update(over)  # partials / reduced may be given
-    return A.arrms_plan_reduce(CU, None, lim["max_world"], lim["max_tokens"], lim["max_hidden"], b["partials"], W, T,
-                               H, b.get("reduced", b["residual_out"]))
+    return A.arrms_plan_reduce(CU, tuning, lim["max_world"], lim["max_tokens"], lim["max_hidden"], b["partials"], W,
+                               T, H, b.get("reduced", b["residual_out"]))
 
 
 @pytest.mark.parametrize("W,T,H", [(4, 4096, 2048), (8, 16383, 5120), (2, 1, 8), (3, 7, 3), (16, 5, 1000), (11, 3, 2048)])
@@ -471,6 +471,39 @@ def test_line_offset_rows_take_the_scalar_kernel(W, T, H, variant):
         assert rc == A.ARRMS_OK and p["variant"] == A.ARRMS_VARIANT_ROW or H > 8192, (t, p)
     rc, p = plan(4, 2048, 2040, cu=128)                           # 16 rows per CU on 128 CUs
     assert p["variant"] == A.ARRMS_VARIANT_SCALAR
+
+
+# Preloaded kernel arguments: the flat-argument twins serve row, scalar (without the rank
+# loop) and rank-sum calls with W <= 8 from 16 MiB of traffic per call; tuning turns
+# them off (1) or on wherever a twin exists (2).
+@pytest.mark.parametrize("W,T,H,want", [
+    (4, 4096, 2048, 1), (4, 585, 2048, 1), (4, 584, 2048, 0), (4, 1, 2048, 0), (8, 16383, 5120, 1),
+    (8, 8192, 8192, 0), (4, 4096, 2047, 1), (12, 4096, 2048, 0), (8, 1, 8192, 0), (1, 16384, 512, 1),
+    (4, 4096, 2040, 1), (8, 4096, 4095, 0), (7, 4096, 4095, 1),
+])
+def test_kernarg_preload_plan(W, T, H, want):
+    rc, p = plan(W, T, H)
+    assert rc == A.ARRMS_OK and p["kernarg_preload"] == want, (W, T, H, p)
+    twin = W <= 8 and (p["variant"] == A.ARRMS_VARIANT_ROW or
+                       (p["variant"] == A.ARRMS_VARIANT_SCALAR and not p["rank_loop"]))
+    assert plan(W, T, H, tuning=A.arrms_tuning_t.make(kernarg_preload=1))[1]["kernarg_preload"] == 0
+    assert plan(W, T, H, tuning=A.arrms_tuning_t.make(kernarg_preload=2))[1]["kernarg_preload"] == int(twin)
+    assert 2 * T * H * (W + 3) + 2 * H >= 16 << 20 or not want
+
+
+def test_kernarg_preload_reduce_plan():
+    for W, T, want in ((4, 4096, 1), (2, 16, 0), (8, 16384, 0), (5, 16384, 1), (12, 4096, 0)):
+        rc, p = rplan(W, T, 2048)
+        assert rc == A.ARRMS_OK and p["kernarg_preload"] == want, (W, T, p)
+    assert rplan(4, 4096, 2048, tuning=A.arrms_tuning_t.make(kernarg_preload=1))[1]["kernarg_preload"] == 0
+    assert rplan(2, 16, 2048, tuning=A.arrms_tuning_t.make(kernarg_preload=2))[1]["kernarg_preload"] == 1
+    assert rplan(8, 16384, 2048, tuning=A.arrms_tuning_t.make(kernarg_preload=2))[1]["kernarg_preload"] == 0
+
+
+def test_kernarg_preload_tuning_range():
+    for bad in (-1, 3):
+        rc, _ = plan(4, 4096, 2048, tuning=A.arrms_tuning_t.make(kernarg_preload=bad))
+        assert rc == A.ARRMS_ERR_INVALID_ARG
 
 
 def test_many_ranks_rule_scales_with_cus_and_respects_tuning():

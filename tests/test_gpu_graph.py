@@ -17,10 +17,12 @@ DEV = torch.device("cuda", 0)
 @pytest.mark.parametrize("W,T,H,variant", [(4, 1, 2048, A.ARRMS_VARIANT_AUTO), (4, 16, 2048, A.ARRMS_VARIANT_AUTO),
                                            (8, 1, 8192, A.ARRMS_VARIANT_AUTO), (4, 128, 2048, A.ARRMS_VARIANT_SPLITH),
                                            (4, 300, 2048, A.ARRMS_VARIANT_ROW), (3, 5, 1001, A.ARRMS_VARIANT_AUTO)])
-def test_graph_replays_match_eager(W, T, H, variant):
-    say("case graph W=%d T=%d H=%d variant=%d" % (W, T, H, variant))
+@pytest.mark.parametrize("preload", [0, 2])  # automatic, and the flat-argument twins wherever they exist
+def test_graph_replays_match_eager(W, T, H, variant, preload):
+    say("case graph W=%d T=%d H=%d variant=%d preload=%d" % (W, T, H, variant, preload))
     o = op()
     o.set_variant(variant)
+    o.set_tuning(kernarg_preload=preload)
     try:
         cases = [inputs(W, T, H, seed=400 + i) for i in range(3)]
         xd = torch.empty((W, T, H), dtype=torch.bfloat16, device=DEV)
@@ -55,31 +57,37 @@ def test_graph_replays_match_eager(W, T, H, variant):
         del g
     finally:
         o.set_variant(A.ARRMS_VARIANT_AUTO)
+        o.set_tuning()
 
 
-def test_reduce_in_graph():
-    say("case graph reduce")
+@pytest.mark.parametrize("preload", [0, 2])
+def test_reduce_in_graph(preload):
+    say("case graph reduce preload=%d" % preload)
     x, r, w = inputs(8, 64, 5120, seed=410)
     xd = x.to(DEV)
     out = torch.empty((64, 5120), dtype=torch.bfloat16, device=DEV)
     o = op()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        o.reduce(xd, out)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        o.reduce(xd, out)
-    want = reference(x, r, w, 1e-6)["reduced"]
-    for rep in range(4):
-        out.fill_(0)
+    o.set_tuning(kernarg_preload=preload)
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            o.reduce(xd, out)
+        torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        assert np.array_equal(synth.bits(out.cpu()), want)
-    del g
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            o.reduce(xd, out)
+        want = reference(x, r, w, 1e-6)["reduced"]
+        for rep in range(4):
+            out.fill_(0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(synth.bits(out.cpu()), want)
+        del g
+    finally:
+        o.set_tuning()
 
 
 @pytest.mark.parametrize("W,T,H", [(8, 16, 8192), (4, 64, 2048), (3, 5, 1001)])

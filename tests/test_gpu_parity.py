@@ -148,6 +148,20 @@ def test_line_offset_rows_scalar_plan(W, T, H):
     assert plan["variant"] == SCALAR and plan["elems_per_load"] == 4 and plan["rank_loop"] == 0
 
 
+# Kernels with preloaded arguments (the flat-argument twins) and kernels taking one
+# argument block: the same bits, each forced on row kernels of several lane layouts and
+# scalar kernels of every load width (specialised W <= 8), small and large calls.
+@pytest.mark.parametrize("W,T,H,variant", [(1, 300, 2048, ROW), (2, 1000, 1024, ROW), (3, 37, 8192, ROW),
+                                           (4, 4096, 2048, ROW), (5, 64, 5120, ROW), (6, 33, 2048, ROW),
+                                           (7, 100, 4096, ROW), (8, 129, 16384, ROW), (4, 130, 2047, SCALAR),
+                                           (3, 77, 2046, SCALAR), (8, 200, 2044, SCALAR), (1, 65, 8193, SCALAR),
+                                           (4, 4096, 2040, AUTO)])
+@pytest.mark.parametrize("preload", [1, 2])
+def test_kernarg_preload_paths(W, T, H, variant, preload):
+    plan, _ = parity(W, T, H, variant=variant, tuning=dict(kernarg_preload=preload), seed=W + T + H + preload)
+    assert plan["kernarg_preload"] == (preload == 2), plan
+
+
 def _shifted(t, off, dev):
     """A copy of CPU tensor t on the GPU, starting `off` bytes past a 256-byte boundary."""
     buf = torch.zeros(t.numel() + 16, dtype=torch.bfloat16, device=dev)

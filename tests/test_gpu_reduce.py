@@ -142,3 +142,29 @@ def test_reduce_tunings(W, vpt, k):
     finally:
         o.set_tuning()
     assert np.array_equal(got, reference(x, res, w, 1e-6)["reduced"])
+
+
+# Rank-sum kernels with preloaded arguments (the flat-argument twins) and with one
+# argument block, each forced: every load width (tuned narrower on aligned tensors),
+# 1, 2 and 4 vectors per lane, a head and tail from an offset, W = 1..8.
+@pytest.mark.parametrize("W,vpt,elems,off", [(1, 1, 8, 0), (2, 2, 8, 0), (4, 4, 8, 0), (5, 0, 4, 0), (6, 0, 2, 0),
+                                             (8, 0, 1, 0), (3, 1, 8, 6), (7, 2, 8, 2)])
+@pytest.mark.parametrize("preload", [1, 2])
+def test_reduce_kernarg_preload_paths(W, vpt, elems, off, preload):
+    T, H = 301, 1000
+    say("case reduce preload=%d W=%d vpt=%d elems=%d +%d" % (preload, W, vpt, elems, off))
+    x, res, w = inputs(W, T, H, seed=330 + W + elems + preload)
+    parts = [_placed(x[r], off) for r in range(W)]
+    out = _placed(torch.zeros(T, H, dtype=torch.bfloat16), off)
+    tun = dict(kernarg_preload=preload, vec_per_thread=vpt, scalar_elems=elems if elems < 8 else 0)
+    rc, plan = A.arrms_plan_reduce(256, A.arrms_tuning_t.make(**tun), 16, 20000, 65536,
+                                   [p.data_ptr() for p in parts], W, T, H, out.data_ptr())
+    assert rc == A.ARRMS_OK and plan["kernarg_preload"] == (preload == 2) and plan["elems_per_load"] == elems, plan
+    o = op()
+    o.set_tuning(**tun)
+    try:
+        o.reduce(parts, out)
+        torch.cuda.synchronize()
+    finally:
+        o.set_tuning()
+    assert np.array_equal(synth.bits(out.cpu()), reference(x, res, w, 1e-6)["reduced"])
