@@ -970,7 +970,7 @@ def summarize_profiles(run_dir: str, workload: str, out_dir: str = None) -> None
         trace[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     # the headline kernel: the most dispatched library kernel at the headline launch shape
     kname = max((len(v), k) for k, v in trace.items()
-                if k[1] == grid_threads and k[2] == plan["block"] and "kernel<" in k[0])[1][0]
+                if k[1] == grid_threads and k[2] == plan["block"] and ("kernel<" in k[0] or "kernel_flat<" in k[0]))[1][0]
     head = trace[(kname, grid_threads, plan["block"])]
     kkey = (kname, grid_threads)
     mean = {}
