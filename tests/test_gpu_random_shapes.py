@@ -1,7 +1,7 @@
 """Seeded random cases against the oracle: world sizes, token counts, hidden sizes
 (multiples of 8 and not), forced variants, tensors placed at 2-, 4-, 8-, 12- and
-16-byte offsets (16-byte vector paths and every scalar load width), in-place residual, and
-the rank sum alone.  Every element is compared, to the parity bar of
+16-byte offsets (16-byte vector paths and every scalar load width), in-place residual,
+kernels with preloaded arguments forced in every other case, and the rank sum alone.  Every element is compared, to the parity bar of
 tests/gpu_util.py."""
 import os
 
@@ -64,8 +64,9 @@ def _placed(t, off_bytes):
 
 @pytest.mark.parametrize("i,W,T,H,offs,inplace,variant,seed", CASES, ids=["case%d" % c[0] for c in CASES])
 def test_random_case(i, W, T, H, offs, inplace, variant, seed):
-    where = "random case %d: W=%d T=%d H=%d offsets=%s inplace=%s variant=%s seed=%d" % (
-        i, W, T, H, offs, inplace, VNAMES[variant], seed)
+    preload = 2 if i % 2 else 0  # odd cases: the flat-argument twins wherever they exist
+    where = "random case %d: W=%d T=%d H=%d offsets=%s inplace=%s variant=%s seed=%d preload=%d" % (
+        i, W, T, H, offs, inplace, VNAMES[variant], seed, preload)
     say(where)
     x, res, w = inputs(W, T, H, seed=seed, outlier_p=0.01 if i % 3 == 0 else 0.0)
     xs = [_placed(x[r], offs[r]) for r in range(W)]
@@ -75,6 +76,7 @@ def test_random_case(i, W, T, H, offs, inplace, variant, seed):
     no = _placed(torch.zeros_like(res), offs[W + 3])
     o = op()
     o.set_variant(variant)
+    o.set_tuning(kernarg_preload=preload)
     try:
         plan = o.plan(xs, rs, ws, 1e-6, ro, no)
         if variant != A.ARRMS_VARIANT_AUTO:
@@ -83,6 +85,7 @@ def test_random_case(i, W, T, H, offs, inplace, variant, seed):
         torch.cuda.synchronize()
     finally:
         o.set_variant(A.ARRMS_VARIANT_AUTO)
+        o.set_tuning()
     n = assert_parity(synth.bits(ro.cpu()), synth.bits(no.cpu()), reference(x, res, w, 1e-6), where)
     say("  plan %s, norm_out not bit-identical: %d" % (plan, n))
 
@@ -92,12 +95,18 @@ REDUCE_CASES = [(i, W, T, H, offs[:W] + (offs[W + 2],), 2000 + i) for i, W, T, H
 
 @pytest.mark.parametrize("i,W,T,H,offs,seed", REDUCE_CASES, ids=["reduce%d" % c[0] for c in REDUCE_CASES])
 def test_random_reduce_case(i, W, T, H, offs, seed):
-    say("random reduce case %d: W=%d T=%d H=%d offsets=%s seed=%d" % (i, W, T, H, offs, seed))
+    preload = 2 if i % 2 else 0
+    say("random reduce case %d: W=%d T=%d H=%d offsets=%s seed=%d preload=%d" % (i, W, T, H, offs, seed, preload))
     x, res, w = inputs(W, T, H, seed=seed)
     xs = [_placed(x[r], offs[r]) for r in range(W)]
     out = _placed(torch.zeros_like(res), offs[W])
-    op().reduce(xs, out)
-    torch.cuda.synchronize()
+    o = op()
+    o.set_tuning(kernarg_preload=preload)
+    try:
+        o.reduce(xs, out)
+        torch.cuda.synchronize()
+    finally:
+        o.set_tuning()
     want = reference(x, res, w, 1e-6)["reduced"]
     got = synth.bits(out.cpu())
     assert np.array_equal(got, want), "reduced differs in %d elements" % int((got != want).sum())
