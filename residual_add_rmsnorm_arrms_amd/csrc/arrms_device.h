@@ -145,15 +145,26 @@ template <> struct Buf<8> {
 // the i-th workgroup an XCD receives takes logical block (8 * (i / K) + x) * K
 // + i % K (x = its XCD): runs of K consecutive blocks (rows) stay on one XCD,
 // and at any moment the 8 XCDs work on neighbouring runs.  K = 0 keeps the
-// hardware's round-robin order.  Returns -1 for padding blocks past `blocks`.
+// hardware's round-robin order.  Returns -1 for padding blocks past `blocks`.  K is
+// uniform, so the power-of-two test is one scalar branch; the division it saves is
+// about 40 scalar instructions at the start of every workgroup (measured on MI355X:
+// 0.2 % faster at W=4 H=2048 T=4096, 0.7 % at T=1024, 1 % at W=1).
 __device__ __forceinline__ int logical_block(int xcd_chunk, int blocks) {
     const int b = blockIdx.x;
     const int k = xcd_chunk;
     if (k == 0) return b;
     const int x = b & 7;
     const int i = b >> 3;
-    const int j = i / k;
-    const int l = (j * 8 + x) * k + (i - j * k);
+    int j, r;  // i = j * k + r
+    if ((k & (k - 1)) == 0) {  // every automatic K: a shift and a mask instead of a division
+        const int sh = __builtin_ctz(static_cast<unsigned>(k));
+        j = i >> sh;
+        r = i & (k - 1);
+    } else {
+        j = i / k;
+        r = i - j * k;
+    }
+    const int l = (j * 8 + x) * k + r;
     return l < blocks ? l : -1;
 }
 
