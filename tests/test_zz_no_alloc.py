@@ -64,7 +64,9 @@ class Case:
 
 @pytest.mark.parametrize("big,small", [((8, 64, 8192), (8, 16, 8192)),     # split-H: the scratch is used
                                        ((4, 48, 32768), (4, 5, 32768)),    # split-H beyond the row kernels
-                                       ((4, 4096, 2048), (4, 7, 2048)),    # row variant: no scratch
+                                       ((4, 4096, 2048), (4, 7, 2048)),    # row variant, preloaded arguments
+                                       #   then one argument block: no scratch
+                                       ((4, 4096, 2047), (4, 3, 2047)),    # scalar variant, likewise
                                        ((3, 300, 1001), (3, 2, 1001)),     # scalar variant: no scratch
                                        ((12, 1024, 4096), (12, 9, 4096))])  # the rank loop, then the row kernel
 def test_two_calls_match_arrms_fused(big, small):
